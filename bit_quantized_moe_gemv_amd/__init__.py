@@ -1,0 +1,230 @@
+"""Python binding of libbqmoe.so, the gfx950 routed-expert MoE layer with
+MXFP4 / VQ-coded experts.
+
+This module only marshals arguments: every step of the layer runs in the HIP
+kernels behind the C ABI declared in include/bqmoe.h.  PyTorch supplies the
+device memory (tensor data pointers) and the stream; there is no CPU or
+PyTorch fallback -- if the library is missing, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbqmoe.so")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_EHIP = -4
+
+MOE_FMT_MXFP4 = 1
+MOE_FMT_VQ13R8 = 2
+
+MOE_PATH_AUTO = 0
+MOE_PATH_DECODE = 1
+MOE_PATH_PREFILL = 2
+MOE_DECODE_MAX_TOKENS = 16
+
+EXPORTED_SYMBOLS = (
+    "moe_packed_size",
+    "moe_workspace_size",
+    "moe_layer_create",
+    "moe_layer_forward",
+    "moe_layer_routing",
+    "moe_layer_last_path",
+    "moe_layer_destroy",
+    "moe_status_str",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+        self.status = status
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("format", ctypes.c_int32),
+        ("force_path", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbqmoe.so (built in-tree by build.py).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python bit_quantized_moe_gemv_amd/build.py or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(moe_layer_desc)
+    lib.moe_packed_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_packed_size.restype = ctypes.c_int
+    lib.moe_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_workspace_size.restype = ctypes.c_int
+    lib.moe_layer_create.argtypes = [D, P, ctypes.c_size_t, ctypes.POINTER(P)]
+    lib.moe_layer_create.restype = ctypes.c_int
+    lib.moe_layer_forward.argtypes = [P, P, ctypes.c_int32, P, P, P, P]
+    lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_routing.argtypes = [P, P, P, P, P, P, P, P]
+    lib.moe_layer_routing.restype = ctypes.c_int
+    lib.moe_layer_last_path.argtypes = [P]
+    lib.moe_layer_last_path.restype = ctypes.c_int
+    lib.moe_layer_destroy.argtypes = [P]
+    lib.moe_layer_destroy.restype = None
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+def _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path) -> moe_layer_desc:
+    return moe_layer_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+
+
+def packed_size(hidden, inter, n_experts, top_k, max_tokens=1, fmt=MOE_FMT_MXFP4,
+                force_path=MOE_PATH_AUTO) -> int:
+    b = ctypes.c_size_t(0)
+    rc = load_library().moe_packed_size(
+        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)),
+        ctypes.byref(b))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_packed_size")
+    return b.value
+
+
+def workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt=MOE_FMT_MXFP4,
+                   force_path=MOE_PATH_AUTO) -> int:
+    b = ctypes.c_size_t(0)
+    rc = load_library().moe_workspace_size(
+        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)),
+        ctypes.byref(b))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_workspace_size")
+    return b.value
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+@dataclass
+class Routing:
+    topk_idx: object
+    topk_w: object
+    counts: object
+    offsets: object
+    perm: object
+    logits: object
+
+
+class MoeLayer:
+    """One routed-expert layer handle with a torch-allocated workspace.
+
+    forward(x, router_w, packed, out=None) runs the whole layer on the
+    current torch stream; x is a [T, hidden] bfloat16 CUDA tensor, router_w a
+    [n_experts, hidden] float32 tensor, packed a uint8 tensor in the layer's
+    packed format; the result is a [T, hidden] float32 tensor."""
+
+    def __init__(self, hidden, inter, n_experts, top_k, max_tokens, fmt=MOE_FMT_MXFP4,
+                 force_path=MOE_PATH_AUTO, device="cuda"):
+        import torch
+
+        self._lib = load_library()
+        self.desc = _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self.max_tokens, self.fmt, self.force_path = max_tokens, fmt, force_path
+        ws_bytes = workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p(0)
+        rc = self._lib.moe_layer_create(ctypes.byref(self.desc), _ptr(self.workspace), ws_bytes,
+                                        ctypes.byref(h))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layer_create")
+        self._handle = h
+        self._last_T = 0
+
+    @property
+    def packed_bytes(self) -> int:
+        return packed_size(self.hidden, self.inter, self.n_experts, self.top_k, self.max_tokens,
+                           self.fmt, self.force_path)
+
+    def forward(self, x, router_w, packed, out=None, stream=None):
+        import torch
+
+        T = int(x.shape[0])
+        if out is None:
+            out = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(x.device)
+        rc = self._lib.moe_layer_forward(self._handle, _ptr(x), T, _ptr(router_w), _ptr(packed),
+                                         _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layer_forward")
+        self._last_T = T
+        return out
+
+    __call__ = forward
+
+    def forward_raw(self, x_ptr: int, T: int, router_ptr: int, packed_ptr: int, out_ptr: int,
+                    stream_ptr: int) -> int:
+        """Pointer-level call (no checks); returns the status code."""
+        return self._lib.moe_layer_forward(self._handle, x_ptr, T, router_ptr, packed_ptr,
+                                           out_ptr, ctypes.c_void_p(stream_ptr))
+
+    def routing(self, stream=None) -> Routing:
+        import torch
+
+        T, k, E = self._last_T, self.top_k, self.n_experts
+        dev = self.workspace.device
+        r = Routing(
+            topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+            topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+            logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+        )
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        rc = self._lib.moe_layer_routing(self._handle, _ptr(r.topk_idx), _ptr(r.topk_w),
+                                         _ptr(r.counts), _ptr(r.offsets), _ptr(r.perm),
+                                         _ptr(r.logits), ctypes.c_void_p(stream.cuda_stream))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layer_routing")
+        return r
+
+    def last_path(self) -> int:
+        return self._lib.moe_layer_last_path(self._handle)
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            self._lib.moe_layer_destroy(self._handle)
+            self._handle = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,213 @@
+// abi.cpp -- the exported C entry points of libbqmoe.so: argument validation,
+// workspace carving and the launch sequence of one forward pass.
+#include <new>
+
+#include "../../include/bqmoe.h"
+#include "moe_internal.h"
+
+using namespace bqmoe;
+
+struct moe_layer {
+    moe_layer_desc desc;
+    Shape shape;
+    void *ws_base;
+    size_t ws_bytes;
+    Workspace ws;
+    int last_T;
+    int last_path;
+};
+
+namespace bqmoe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(const Shape &s, int tmax) {
+    const size_t R = (size_t)tmax * s.K;
+    size_t b = 0;
+    b += align256((size_t)tmax * s.E * 4);  // logits
+    b += align256(R * 4);                   // idx
+    b += align256(R * 4);                   // w
+    b += align256((size_t)s.E * 4);         // counts
+    b += align256((size_t)(s.E + 1) * 4);   // offsets
+    b += align256((size_t)(s.E + 1) * 4);   // active
+    b += align256(R * 4);                   // perm
+    b += align256(R * 4);                   // inv
+    b += align256((size_t)(s.H / 16) * 4);  // sync
+    b += align256(R * s.I * 4);             // h
+    b += align256(R * s.H * 4);             // y
+    return b;
+}
+
+void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
+    const size_t R = (size_t)tmax * s.K;
+    char *p = static_cast<char *>(base);
+    auto take = [&](size_t bytes) {
+        char *r = p;
+        p += align256(bytes);
+        return r;
+    };
+    ws->logits = reinterpret_cast<float *>(take((size_t)tmax * s.E * 4));
+    ws->idx = reinterpret_cast<int32_t *>(take(R * 4));
+    ws->w = reinterpret_cast<float *>(take(R * 4));
+    ws->counts = reinterpret_cast<int32_t *>(take((size_t)s.E * 4));
+    ws->offsets = reinterpret_cast<int32_t *>(take((size_t)(s.E + 1) * 4));
+    ws->active = reinterpret_cast<int32_t *>(take((size_t)(s.E + 1) * 4));
+    ws->perm = reinterpret_cast<int32_t *>(take(R * 4));
+    ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
+    ws->sync = reinterpret_cast<uint32_t *>(take((size_t)(s.H / 16) * 4));
+    ws->h = take(R * s.I * 4);
+    ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
+}
+
+}  // namespace bqmoe
+
+static int check_desc(const moe_layer_desc *d, Shape *s) {
+    if (!d) return MOE_EINVAL;
+    if (d->hidden < 256 || d->hidden > 16384 || d->hidden % 256) return MOE_EINVAL;
+    if (d->inter < 128 || d->inter > 16384) return MOE_EINVAL;
+    if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_EINVAL;
+    if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_EINVAL;
+    if (d->max_tokens < 1 || d->max_tokens > 65536) return MOE_EINVAL;
+    if (d->force_path < MOE_PATH_AUTO || d->force_path > MOE_PATH_PREFILL) return MOE_EINVAL;
+    if (d->format == MOE_FMT_MXFP4) {
+        if (d->inter % 128) return MOE_EINVAL;
+    } else if (d->format == MOE_FMT_VQ13R8) {
+        if (d->inter % 256) return MOE_EINVAL;
+        return MOE_EUNSUPPORTED;  // VQ kernels not built yet
+    } else {
+        return MOE_EINVAL;
+    }
+    // decode kernels hold one wave's packed bytes in registers
+    if (d->force_path != MOE_PATH_PREFILL && (d->hidden > 8192 || d->inter > 2048))
+        return MOE_EUNSUPPORTED;
+    if (s) {
+        s->H = d->hidden;
+        s->I = d->inter;
+        s->E = d->n_experts;
+        s->K = d->top_k;
+        s->fmt = d->format;
+        const size_t H = (size_t)d->hidden, I = (size_t)d->inter;
+        if (d->format == MOE_FMT_MXFP4) {
+            s->expert_bytes = 3 * I * H * 17 / 32;
+            s->books_bytes = 0;
+        } else {
+            s->expert_bytes = 3 * I * H * 21 / 64 + 2 * (2 * I + H);
+            s->books_bytes = kVqBooksBytes;
+        }
+    }
+    return MOE_OK;
+}
+
+static bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+int moe_packed_size(const moe_layer_desc *desc, size_t *bytes) {
+    Shape s;
+    const int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_EINVAL;
+    *bytes = s.books_bytes + s.expert_bytes * (size_t)s.E;
+    return MOE_OK;
+}
+
+int moe_workspace_size(const moe_layer_desc *desc, size_t *bytes) {
+    Shape s;
+    const int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_EINVAL;
+    *bytes = workspace_bytes(s, desc->max_tokens);
+    return MOE_OK;
+}
+
+int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
+                     moe_layer **out) {
+    if (!out) return MOE_EINVAL;
+    *out = nullptr;
+    Shape s;
+    const int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MOE_EWORKSPACE;
+    if (ws_bytes < workspace_bytes(s, desc->max_tokens)) return MOE_EWORKSPACE;
+    moe_layer *L = new (std::nothrow) moe_layer;
+    if (!L) return MOE_EINVAL;
+    L->desc = *desc;
+    L->shape = s;
+    L->ws_base = workspace;
+    L->ws_bytes = ws_bytes;
+    carve_workspace(s, desc->max_tokens, workspace, &L->ws);
+    L->last_T = 0;
+    L->last_path = MOE_EINVAL;
+    *out = L;
+    return MOE_OK;
+}
+
+int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *router_w,
+                      const void *packed_experts, float *out, void *hip_stream) {
+    if (!L) return MOE_EINVAL;
+    if (T < 1 || T > L->desc.max_tokens) return MOE_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(router_w) || !aligned16(packed_experts) ||
+        !aligned16(out))
+        return MOE_EINVAL;
+    int path = L->desc.force_path;
+    if (path == MOE_PATH_AUTO) path = (T <= kDecodeMaxTokens) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_DECODE && T > kDecodeMaxTokens) return MOE_EINVAL;
+    const Shape &s = L->shape;
+    const Workspace &ws = L->ws;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    const uint8_t *packed = static_cast<const uint8_t *>(packed_experts);
+
+    hipError_t err = launch_router(s, x, router_w, T, ws.logits, st);
+    if (path == MOE_PATH_DECODE) {
+        if (err == hipSuccess) err = launch_route_small(s, T, ws, st);
+        if (err == hipSuccess) err = launch_decode_gateup(s, T, x, packed, ws, st);
+        if (err == hipSuccess) err = launch_decode_down(s, T, packed, ws, out, st);
+    } else {
+        if (err == hipSuccess) err = launch_topk(s, T, ws, st);
+        if (err == hipSuccess) err = launch_permute(s, T, ws, st);
+        if (err == hipSuccess) err = launch_prefill_gateup(s, T, x, packed, ws, st);
+        if (err == hipSuccess) err = launch_prefill_down(s, T, packed, ws, st);
+        if (err == hipSuccess) err = launch_combine(s, T, ws, out, st);
+    }
+    if (err != hipSuccess) return MOE_EHIP;
+    L->last_T = T;
+    L->last_path = path;
+    return MOE_OK;
+}
+
+int moe_layer_routing(moe_layer *L, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                      int32_t *offsets, int32_t *perm, float *logits, void *hip_stream) {
+    if (!L || L->last_T < 1) return MOE_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const Shape &s = L->shape;
+    const size_t T = (size_t)L->last_T, R = T * s.K;
+    struct { void *dst; const void *src; size_t bytes; } cp[] = {
+        {topk_idx, L->ws.idx, R * 4},       {topk_w, L->ws.w, R * 4},
+        {counts, L->ws.counts, (size_t)s.E * 4}, {offsets, L->ws.offsets, (size_t)(s.E + 1) * 4},
+        {perm, L->ws.perm, R * 4},          {logits, L->ws.logits, T * s.E * 4},
+    };
+    for (auto &c : cp) {
+        if (!c.dst) continue;
+        if (hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int moe_layer_last_path(const moe_layer *L) { return L && L->last_T > 0 ? L->last_path : MOE_EINVAL; }
+
+void moe_layer_destroy(moe_layer *L) { delete L; }
+
+const char *moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported shape or format";
+        case MOE_EWORKSPACE: return "workspace missing or too small";
+        case MOE_EHIP: return "HIP launch or runtime error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// moe_internal.h -- shared definitions of the gfx950 MoE layer library:
+// workspace carving, launcher declarations and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bqmoe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 256;
+constexpr int kDecodeMaxTokens = 16;
+constexpr int kVqEntries = 8192;
+constexpr int kVqResEntries = 256;
+constexpr size_t kVqBooksBytes = (size_t)(kVqEntries + kVqResEntries) * 8 * 2;
+
+// Shapes of one layer.
+struct Shape {
+    int H, I, E, K;      // hidden, intermediate, experts, top-k
+    int fmt;
+    size_t expert_bytes;  // bytes of one expert in the packed buffer
+    size_t books_bytes;   // bytes before expert 0 (VQ books)
+};
+
+// Device pointers carved out of the caller's workspace.
+struct Workspace {
+    float *logits;     // [Tmax][E]
+    int32_t *idx;      // [Tmax][K]
+    float *w;          // [Tmax][K]
+    int32_t *counts;   // [E]
+    int32_t *offsets;  // [E+1]
+    int32_t *active;   // [1 + E]: n_active, then active experts ascending
+    int32_t *perm;     // [Rmax]
+    int32_t *inv;      // [Rmax]
+    uint32_t *sync;    // [H/16] arrival counters of the decode combine
+    void *h;           // [Rmax][I] fp32 (decode) or two [Rmax][I] bf16 arrays (prefill)
+    float *y;          // [Rmax][H] fp32 per-route expert outputs
+};
+
+size_t workspace_bytes(const Shape &s, int tmax);
+void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws);
+
+// ---- launchers (each returns hipSuccess or the launch error) ----
+hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
+                         hipStream_t st);
+hipError_t launch_route_small(const Shape &s, int T, const Workspace &ws, hipStream_t st);
+hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st);
+hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_t st);
+hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
+                                const Workspace &ws, hipStream_t st);
+hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
+                              float *out, hipStream_t st);
+hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
+                                 const Workspace &ws, hipStream_t st);
+hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
+                               hipStream_t st);
+hipError_t launch_combine(const Shape &s, int T, const Workspace &ws, float *out, hipStream_t st);
+
+// ---- device helpers ----
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// E8M0 exponent byte (1..254) as the fp32 scale 2^(e-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// Four packed fp4 bytes (one dword) -> eight bf16, each times `scale`.
+// Byte b of the dword holds columns 2b (low nibble) and 2b+1 (high nibble).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
+    union { bf16x8 v8; bf16x2 v2[4]; } r;
+    r.v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0);
+    r.v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 1);
+    r.v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
+    r.v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
+    return r.v8;
+}
+
+__device__ __forceinline__ float wave_sum_xor(float v, int from_mask) {
+    for (int m = from_mask; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+}  // namespace bqmoe

@@ -1,0 +1,145 @@
+/*
+ * bqmoe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer with
+ * block-quantized experts.
+ *
+ * The layer (MiMo-V2.6-Flash-RL shape: 256 routed experts, 8 active per token,
+ * no shared expert -- TrevorJS GGUF card, "Architecture notes"; hidden 4096,
+ * expert intermediate 2048) computes for every token t
+ *
+ *   l      = x_t . Wr^T                    fp32 router (F32 router: savrn
+ *                                          card, "Quantization targets")
+ *   idx    = top-k experts by l (ties to the lower index)
+ *   w      = softmax over the k selected logits
+ *   out[t] = sum_s w[s] * D_e (silu(G_e x_t) * (U_e x_t)),  e = idx[s]
+ *
+ * with fp32 accumulation throughout (expert intermediates exceed fp16's 65504:
+ * TrevorJS card, "Recipe", and benthecarman EXL3 card, "Bitrate").
+ *
+ * Every entry point returns an int status (MOE_OK or a negative code); no C++
+ * exception crosses this boundary.  Pointers marked "device" are HIP device
+ * addresses (for example torch tensors' data_ptr()); "host" pointers are
+ * ordinary memory.  The library never allocates or frees device memory: the
+ * caller owns x, router_w, packed_experts, out and the workspace.
+ */
+#ifndef BQMOE_H
+#define BQMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_layer moe_layer; /* opaque handle */
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* bad argument: null/misaligned pointer, size out of range */
+    MOE_EUNSUPPORTED = -2, /* shape or format this build does not implement */
+    MOE_EWORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_size */
+    MOE_EHIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Packed expert formats.
+ *
+ * MOE_FMT_MXFP4 (E2M1 elements, two per byte, one E8M0 exponent per 32
+ * consecutive weights of a row -- TrevorJS card, "Architecture notes"):
+ *   packed = n_experts experts back to back, each 3*inter*hidden*17/32 bytes:
+ *   [gate/up codes][gate/up scales][down codes][down scales].  gate/up is one
+ *   matrix of 2*inter rows (rows [0,inter) gate, [inter,2*inter) up) by hidden
+ *   columns; down is hidden rows by inter columns.  A matrix of N rows and K
+ *   columns is stored as tiles of 16 rows x 32 columns, tile (n/16, k/32) at
+ *   index (n/16)*(K/32) + k/32; a tile is 256 code bytes (tile row r at bytes
+ *   16r..16r+15, column c in byte c/2, even c in the low nibble) and, in the
+ *   scale region, 16 bytes (one E8M0 per tile row).  Weight =
+ *   E2M1(code) * 2^(scale-127).  This build supports scale bytes 1..254.
+ *
+ * MOE_FMT_VQ13R8 (8-dim vector codes: a 13-bit index -- 12-bit stream plus a
+ * 1-bit plane -- into a per-layer book, an 8-bit index into a 256-entry
+ * residual book, and an F16 gain per row -- Baekpica VQ card, "Recipe"):
+ *   packed = [Cb: 8192 x 8 fp16][Rb: 256 x 8 fp16] then n_experts experts of
+ *   3*inter*hidden*21/64 + 2*(2*inter + hidden) bytes:
+ *   [gu code12][gu plane][gu res][gu gain][dn code12][dn plane][dn res][dn gain].
+ *   Tiles are 16 rows x 256 columns (512 vectors); vector (tile row r, vector
+ *   column j) is at stream position ((j/8)*16 + r)*8 + j%8 of its tile; code12
+ *   is a little-endian 12-bit stream, plane a little-endian bit stream (bit 12
+ *   of the index), res one byte per vector; gains are one fp16 per row.
+ *   Weight w[n][8v+d] = gain[n] * (Cb[i13][d] + Rb[i8][d]).
+ */
+enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2 };
+
+/* Path selection: AUTO uses the weight-streaming decode kernels for batches of
+ * at most MOE_DECODE_MAX_TOKENS tokens and the grouped-GEMM prefill kernels
+ * above that; DECODE and PREFILL force one of them (DECODE requires
+ * T <= MOE_DECODE_MAX_TOKENS). */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+#define MOE_DECODE_MAX_TOKENS 16
+
+typedef struct {
+    int32_t hidden;     /* H: multiple of 256 */
+    int32_t inter;      /* I: multiple of 128 (MXFP4) or 256 (VQ13R8) */
+    int32_t n_experts;  /* E: 1..256 */
+    int32_t top_k;      /* k: 1..8 and k <= E */
+    int32_t max_tokens; /* largest T a forward call may pass: 1..65536 */
+    int32_t format;     /* MOE_FMT_* */
+    int32_t force_path; /* MOE_PATH_* */
+} moe_layer_desc;
+
+/* Size in bytes of packed_experts for this descriptor (host out-pointer). */
+int moe_packed_size(const moe_layer_desc *desc, size_t *bytes);
+
+/* Size in bytes of the device workspace a handle needs (host out-pointer). */
+int moe_workspace_size(const moe_layer_desc *desc, size_t *bytes);
+
+/* Validate desc and bind a caller-owned device workspace (256-byte aligned,
+ * at least moe_workspace_size bytes, kept alive until moe_layer_destroy).
+ * Writes a new handle to *out.  Makes no device call. */
+int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
+                     moe_layer **out);
+
+/* One forward pass, enqueued on hip_stream (a hipStream_t; NULL = the null
+ * stream).  Asynchronous: returns after the last launch, with no host sync.
+ *   x_bf16         device, [T][hidden] bfloat16, row-major, 16-byte aligned
+ *   T              1..max_tokens
+ *   router_w       device, [n_experts][hidden] fp32, row-major, 16-byte aligned
+ *   packed_experts device, moe_packed_size bytes in desc->format, 16-byte aligned
+ *   out            device, [T][hidden] fp32, row-major, 16-byte aligned;
+ *                  fully overwritten
+ * The router logit of (t, e) is summed in a fixed order, so routing is
+ * reproducible bit for bit: partial c (0..63) accumulates columns k with
+ * (k/4) mod 64 == c in ascending k with fused multiply-adds from +0, and the
+ * 64 partials are added as a pairwise tree of adjacent blocks.
+ * A handle is not reentrant: calls sharing a handle share its workspace and
+ * must be ordered (one stream at a time).  Non-finite inputs are outside the
+ * contract.  Device faults surface at the caller's next synchronisation. */
+int moe_layer_forward(moe_layer *layer, const void *x_bf16, int32_t T, const float *router_w,
+                      const void *packed_experts, float *out, void *hip_stream);
+
+/* Copy the routing of the last forward into caller device buffers (any may be
+ * NULL to skip), enqueued on hip_stream:
+ *   topk_idx [T][k] int32 (slot order: logit descending, index ascending)
+ *   topk_w   [T][k] fp32 softmax weights
+ *   counts   [n_experts] int32 routes per expert
+ *   offsets  [n_experts+1] int32 exclusive prefix sum of counts
+ *   perm     [T*k] int32 route ids r = t*k+s sorted by (expert, token)
+ *   logits   [T][n_experts] fp32 router logits
+ * Returns MOE_EINVAL if no forward has been issued on the handle. */
+int moe_layer_routing(moe_layer *layer, int32_t *topk_idx, float *topk_w, int32_t *counts,
+                      int32_t *offsets, int32_t *perm, float *logits, void *hip_stream);
+
+/* Path the last forward took (MOE_PATH_DECODE or MOE_PATH_PREFILL), or
+ * MOE_EINVAL before the first forward. */
+int moe_layer_last_path(const moe_layer *layer);
+
+/* Release the handle (not the workspace).  NULL is a no-op. */
+void moe_layer_destroy(moe_layer *layer);
+
+/* Static description of a status code. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQMOE_H */

@@ -1,0 +1,66 @@
+"""Helpers for the GPU tests: move seeded numpy inputs to the device, run the
+layer through the C ABI binding, and bring the results back."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import workloads as W
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(x: np.ndarray, wr: np.ndarray, packed: np.ndarray, dev="cuda"):
+    import torch
+
+    xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    wd = torch.from_numpy(np.ascontiguousarray(wr)).to(dev)
+    pd = torch.from_numpy(np.ascontiguousarray(packed)).to(dev)
+    return xd, wd, pd
+
+
+class Runner:
+    """A layer handle sized for a workload plus device copies of its inputs."""
+
+    def __init__(self, wl: W.Workload, force_path: int, max_tokens: int | None = None,
+                 packed: np.ndarray | None = None):
+        import torch
+        import bit_quantized_moe_gemv_amd as bq
+
+        self.wl = wl
+        self.bq = bq
+        self.layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k,
+                                 max_tokens or wl.tokens, wl.fmt, force_path)
+        self.packed_host = W.make_experts(wl) if packed is None else packed
+        self.packed = torch.from_numpy(self.packed_host).to("cuda")
+        self.torch = torch
+
+    def run(self, x: np.ndarray, wr: np.ndarray, canary: bool = True):
+        torch = self.torch
+        xd = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        wd = torch.from_numpy(np.ascontiguousarray(wr)).to("cuda")
+        t, h = x.shape
+        pad = 64 if canary else 0
+        buf = torch.full(((t * h + pad),), 12345.0, dtype=torch.float32, device="cuda")
+        out = buf[:t * h].view(t, h)
+        self.layer.forward(xd, wd, self.packed, out=out)
+        r = self.layer.routing()
+        torch.cuda.synchronize()
+        if canary:
+            tail = buf[t * h:].cpu().numpy()
+            assert np.all(tail == 12345.0), "output canary overwritten"
+        return dict(
+            out=out.cpu().numpy().astype(np.float64),
+            idx=r.topk_idx.cpu().numpy(),
+            w=r.topk_w.cpu().numpy(),
+            counts=r.counts.cpu().numpy(),
+            offsets=r.offsets.cpu().numpy(),
+            perm=r.perm.cpu().numpy(),
+            logits=r.logits.cpu().numpy(),
+            path=self.layer.last_path(),
+        )

@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every entry point include/bqmoe.h
+declares, and rejects bad arguments on the host before any device call.
+CPU only: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_moe_gemv_amd as bq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bqmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bq.LIB_PATH):
+        from bit_quantized_moe_gemv_amd import build
+        build.build()
+    return bq.load_library()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _header_functions() == sorted(bq.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+    nm = os.popen(f"nm -D --defined-only {bq.LIB_PATH}").read()
+    for name in _header_functions():
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_status_strings(lib):
+    assert bq.status_str(0) == "ok"
+    for c in (bq.MOE_EINVAL, bq.MOE_EUNSUPPORTED, bq.MOE_EWORKSPACE, bq.MOE_EHIP):
+        assert bq.status_str(c) and bq.status_str(c) != "unknown status"
+
+
+def test_sizes_for_the_mimo_layer(lib):
+    assert bq.packed_size(4096, 2048, 256, 8) == 3422552064
+    assert bq.packed_size(256, 128, 8, 2) == 417792
+    ws = bq.workspace_size(4096, 2048, 256, 8, 2048)
+    r = 2048 * 8
+    assert ws >= r * (2048 * 4 + 4096 * 4)
+    assert ws < r * (2048 * 4 + 4096 * 4) + 8 * 2**20
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=200), dict(hidden=0), dict(inter=96), dict(n_experts=0), dict(n_experts=300),
+    dict(top_k=0), dict(top_k=9), dict(top_k=9, n_experts=8), dict(max_tokens=0),
+    dict(fmt=7), dict(force_path=5),
+])
+def test_descriptor_validation(lib, bad):
+    d = dict(hidden=256, inter=128, n_experts=8, top_k=2, max_tokens=16, fmt=1, force_path=0)
+    d.update(bad)
+    with pytest.raises(bq.MoeError) as ei:
+        bq.packed_size(**d)
+    assert ei.value.status == bq.MOE_EINVAL
+
+
+def test_top_k_larger_than_experts_rejected(lib):
+    with pytest.raises(bq.MoeError):
+        bq.packed_size(256, 128, 4, 8)
+
+
+def test_create_and_forward_validation_without_device(lib):
+    d = bq.moe_layer_desc(256, 128, 8, 2, 16, 1, 0)
+    ws = bq.workspace_size(256, 128, 8, 2, 16)
+    h = ctypes.c_void_p(0)
+    fake = 0x7F0000000000  # never dereferenced: validation fails or no launch happens
+    assert lib.moe_layer_create(ctypes.byref(d), None, ws, ctypes.byref(h)) == bq.MOE_EWORKSPACE
+    assert lib.moe_layer_create(ctypes.byref(d), fake + 16, ws, ctypes.byref(h)) == bq.MOE_EWORKSPACE
+    assert lib.moe_layer_create(ctypes.byref(d), fake, ws - 1, ctypes.byref(h)) == bq.MOE_EWORKSPACE
+    assert lib.moe_layer_create(ctypes.byref(d), fake, ws, None) == bq.MOE_EINVAL
+    assert lib.moe_layer_create(ctypes.byref(d), fake, ws, ctypes.byref(h)) == bq.MOE_OK
+    try:
+        fw = lib.moe_layer_forward
+        a = fake
+        # T out of range, null and misaligned pointers: rejected before any launch
+        assert fw(h, a, 0, a, a, a, None) == bq.MOE_EINVAL
+        assert fw(h, a, 17, a, a, a, None) == bq.MOE_EINVAL
+        assert fw(h, None, 1, a, a, a, None) == bq.MOE_EINVAL
+        assert fw(h, a + 2, 1, a, a, a, None) == bq.MOE_EINVAL
+        assert fw(h, a, 1, a + 4, a, a, None) == bq.MOE_EINVAL
+        assert fw(h, a, 1, a, a + 8, a, None) == bq.MOE_EINVAL
+        assert fw(h, a, 1, a, a, None, None) == bq.MOE_EINVAL
+        assert fw(None, a, 1, a, a, a, None) == bq.MOE_EINVAL
+        # no forward yet: routing and last_path report EINVAL
+        assert lib.moe_layer_routing(h, None, None, None, None, None, None, None) == bq.MOE_EINVAL
+        assert lib.moe_layer_last_path(h) == bq.MOE_EINVAL
+    finally:
+        lib.moe_layer_destroy(h)
+    lib.moe_layer_destroy(None)
+
+
+def test_forced_decode_rejects_large_batches(lib):
+    d = bq.moe_layer_desc(256, 128, 8, 2, 64, 1, bq.MOE_PATH_DECODE)
+    ws = bq.workspace_size(256, 128, 8, 2, 64, 1, bq.MOE_PATH_DECODE)
+    h = ctypes.c_void_p(0)
+    fake = 0x7F0000000000
+    assert lib.moe_layer_create(ctypes.byref(d), fake, ws, ctypes.byref(h)) == bq.MOE_OK
+    try:
+        assert lib.moe_layer_forward(h, fake, 17, fake, fake, fake, None) == bq.MOE_EINVAL
+    finally:
+        lib.moe_layer_destroy(h)

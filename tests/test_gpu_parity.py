@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.  Routing (logits, top-k indices, counts, offsets,
+permutation) must match bit for bit; the output must satisfy, per token row,
+relative L2 error <= 2e-3 and max |error| <= 1e-2 * rms of the row."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import check_output
+
+pytestmark = pytest.mark.gpu
+
+DEC = 1
+PRE = 2
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_moe_gemv_amd as bq
+    bq.load_library()
+    return torch
+
+
+def _routing_exact(got, ref, wl):
+    assert np.array_equal(got["logits"].view(np.uint32), ref["logits"].view(np.uint32)), \
+        "router logits differ bitwise"
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["perm"], ref["perm"])
+    assert np.max(np.abs(got["w"] - ref["w"])) < 1e-5
+
+
+def _full_check(torch_dev, wl, path, x=None, wr=None, packed=None, max_tokens=None):
+    from gpu_harness import Runner, log
+    import oracle
+    log(f"case {wl.name} T={wl.tokens if x is None else x.shape[0]} path={path}")
+    x = W.make_x(wl) if x is None else x
+    wr = W.make_router(wl) if wr is None else wr
+    run = Runner(wl, path, max_tokens=max_tokens or x.shape[0], packed=packed)
+    got = run.run(x, wr)
+    ref_route = oracle.route(x, wr, wl.top_k)
+    ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k,
+                             run.packed_host, x, wr)
+    assert got["path"] == path
+    _routing_exact(got, ref_route, wl)
+    l2, mx = check_output(got["out"], ref["out"])
+    log(f"  worst row: rel l2 {l2:.2e}, max/rms {mx:.2e}")
+    return got, ref, run
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+def test_tiny_layer(torch_dev, path):
+    _full_check(torch_dev, W.TINY, path)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+@pytest.mark.parametrize("t", [1, 3, 7])
+def test_tiny_ragged_token_counts(torch_dev, path, t):
+    wl = W.TINY.replace(tokens=t, seed=100 + t)
+    _full_check(torch_dev, wl, path)
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+def test_zero_router_sends_all_tokens_to_first_experts(torch_dev, path):
+    """All logits +0: every token picks experts 0..k-1, so two experts hold
+    every route (exercises the multi-chunk loops of both paths)."""
+    wl = W.TINY if path == DEC else W.TINY.replace(tokens=150, seed=11)
+    wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
+    got, ref, _ = _full_check(torch_dev, wl, path, wr=wr)
+    assert got["counts"][:wl.top_k].tolist() == [wl.tokens] * wl.top_k
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+def test_zero_input_gives_zero_output(torch_dev, path):
+    wl = W.TINY
+    x = np.zeros((wl.tokens, wl.hidden), dtype=np.uint16)
+    got, _, _ = _full_check(torch_dev, wl, path, x=x)
+    assert np.all(got["out"] == 0)
+
+
+def test_prefill_ragged_medium(torch_dev):
+    # several 64-token chunks per expert plus ragged tails
+    wl = W.TINY.replace(tokens=333, seed=12)
+    _full_check(torch_dev, wl, PRE)
+
+
+def test_prefill_scaled_tokens_tiny(torch_dev):
+    wl = W.TINY.replace(tokens=64, seed=13, scaled_tokens=4, token_scale=64.0)
+    _full_check(torch_dev, wl, PRE)
+
+
+def test_all_experts_active_k8(torch_dev):
+    wl = W.TINY.replace(top_k=8, name="tiny_k8")
+    for path in (DEC, PRE):
+        _full_check(torch_dev, wl, path)
+
+
+def test_determinism_bitwise(torch_dev):
+    from gpu_harness import Runner
+    for path, wl in ((DEC, W.TINY), (PRE, W.TINY.replace(tokens=200, seed=14))):
+        x, wr = W.make_x(wl), W.make_router(wl)
+        run = Runner(wl, path)
+        a = run.run(x, wr)["out"]
+        b = run.run(x, wr)["out"]
+        assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# full MiMo shape (hidden 4096, intermediate 2048, 256 experts, top-8)
+# ---------------------------------------------------------------------------
+
+_LAYERS = {}
+
+
+def _mimo_layer(seed):
+    if seed not in _LAYERS:
+        _LAYERS.clear()
+        _LAYERS[seed] = W.make_experts(W.DECODE.replace(seed=seed))
+    return _LAYERS[seed]
+
+
+def _sampled_check(torch_dev, wl, path, sample):
+    from gpu_harness import Runner, log
+    import oracle
+    log(f"case {wl.name} T={wl.tokens} path={path} sample={list(sample)}")
+    x, wr = W.make_x(wl), W.make_router(wl)
+    packed = _mimo_layer(wl.seed)
+    run = Runner(wl, path, packed=packed)
+    got = run.run(x, wr)
+    log("  gpu done; oracle routing")
+    ref_route = oracle.route(x, wr, wl.top_k)
+    _routing_exact(got, ref_route, wl)
+    log("  routing exact; oracle outputs")
+    ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, packed, x, wr,
+                             tokens=sample)
+    l2, mx = check_output(got["out"][np.asarray(sample)], ref["out"])
+    log(f"  worst sampled row: rel l2 {l2:.2e}, max/rms {mx:.2e}")
+    assert np.all(np.isfinite(got["out"]))
+    return got
+
+
+def test_mimo_decode_batch1(torch_dev):
+    _sampled_check(torch_dev, W.DECODE, DEC, [0])
+
+
+def test_mimo_verify_batch16_skewed(torch_dev):
+    got = _sampled_check(torch_dev, W.VERIFY, DEC, [0, 5, 15])
+    n_distinct = int((got["counts"] > 0).sum())
+    assert 40 <= n_distinct <= 128
+
+
+def test_mimo_prefill_2048(torch_dev):
+    wl = W.PREFILL
+    scaled = W.scaled_token_ids(wl)
+    sample = sorted(set(scaled[:3].tolist()) | {0, 1000, 2047})
+    got = _sampled_check(torch_dev, wl, PRE, sample)
+    assert got["counts"].sum() == wl.tokens * wl.top_k
