@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer (MXFP4 experts) on one MI355X.
+
+One step = one call of moe_layer_forward over one batch: router, top-8,
+grouping, gate/up + SwiGLU, down projection and weighted combine.  The headline
+workload is decode at batch 1 on the MiMo-shaped layer (hidden 4096,
+intermediate 2048, 256 experts, top-8, 3,422,552,064 bytes of MXFP4 experts).
+
+Cache protocol: the 256 MB last-level cache could hold a decode step's
+111 MB working set, so steps cycle through --layers device copies of the layer
+and every step takes a fresh token; a reused expert is then never still cached.
+
+Prints ONE JSON line (rank 0): metric/value (tokens/s), roofline of the
+dominant kernel (HIP events around each of its launches on its own stream),
+the CPU oracle timed on a bounded sample, and extra workloads (16-token
+verify with skewed routing, 2048-token prefill) with their own rooflines.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_quantized_moe_gemv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _traffic(kernel: str, src: str, launches_units: float):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256") != _src_hash(src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def measured_peaks(torch):
+    """Attainable peaks on this machine: a device-to-device copy and a bf16 GEMM."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    it = 10
+    for _ in range(it):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * it / (time.perf_counter() - t0) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        x @ y
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    it = 20
+    for _ in range(it):
+        x @ y
+    torch.cuda.synchronize()
+    tflops = 2 * m ** 3 * it / (time.perf_counter() - t0) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(copy_gbs, 1), "bf16_matmul_tflops": round(tflops, 1)}
+
+
+class Bench:
+    def __init__(self, args, torch, bq, W):
+        self.args, self.torch, self.bq, self.W = args, torch, bq, W
+        base = W.DECODE
+        log(f"generating the MiMo-shaped MXFP4 layer ({base.packed_bytes} B)")
+        t0 = time.perf_counter()
+        self.host_layer = W.make_experts(base)
+        log(f"  {time.perf_counter() - t0:.1f}s; copying {args.layers} device copies")
+        src = torch.from_numpy(self.host_layer)
+        self.layers = [src.to("cuda") for _ in range(args.layers)]
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+
+    def run(self, wl, steps, warmup, tokens_per_step, profile=True):
+        torch, bq, W = self.torch, self.bq, self.W
+        T = tokens_per_step
+        n_batches = steps + warmup
+        # a fresh batch of tokens for every step
+        xs = []
+        per = 1 if wl.scaled_tokens else max(1, 4096 // T)
+        for off in range(0, n_batches, per):
+            cnt = min(per, n_batches - off)
+            x = W.make_x(wl, tokens=T * cnt, stream_offset=1 + off)
+            xs.append(torch.from_numpy(x.view("int16")).to("cuda").view(torch.bfloat16))
+        xall = torch.cat(xs).view(n_batches, T, wl.hidden)
+        wr = torch.from_numpy(W.make_router(wl)).to("cuda")
+        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt)
+        out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+        st = self.stream.cuda_stream
+        L = len(self.layers)
+        xp = [int(xall[i].data_ptr()) for i in range(n_batches)]
+        lp = [int(t.data_ptr()) for t in self.layers]
+        wp, op = int(wr.data_ptr()), int(out.data_ptr())
+
+        def loop(i0, n):
+            for i in range(i0, i0 + n):
+                rc = layer.forward_raw(xp[i], T, wp, lp[i % L], op, st)
+                if rc != 0:
+                    raise bq.MoeError(rc, "moe_layer_forward")
+
+        loop(0, warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        loop(warmup, steps)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        res = {"steps": steps, "warmup": warmup, "ms_per_step": elapsed * 1e3 / steps,
+               "tokens_per_s": steps * T / elapsed, "path": layer.last_path()}
+        # routing statistics of the last step (distinct experts streamed)
+        r = layer.routing()
+        counts = r.counts.cpu()
+        res["distinct_experts_last_step"] = int((counts > 0).sum())
+        if profile:
+            # second pass over the same steps with event pairs around each kernel
+            layer.set_profiling(steps)
+            loop(warmup, steps)
+            torch.cuda.synchronize()
+            prof = layer.profile_read()
+            layer.set_profiling(0)
+            stages = {}
+            for name in bq.STAGES:
+                v = [p[name] for p in prof if name in p]
+                if v:
+                    stages[name] = sum(v) / len(v) * 1e3  # microseconds
+            res["stage_us"] = {k: round(v, 2) for k, v in stages.items()}
+            res["profiled_ms_per_step"] = sum(stages.values()) / 1e3
+        layer.close()
+        return res
+
+
+def algorithmic(wl, distinct, T):
+    """Algorithmic bytes / flops of the gate/up and down kernels and the whole
+    step.  Per expert: gate/up 2*I*H*17/32 bytes, down H*I*17/32 bytes."""
+    H, I, k = wl.hidden, wl.inter, wl.top_k
+    R = T * k
+    gu_e = 2 * I * H * 17 // 32
+    dn_e = H * I * 17 // 32
+    gateup_bytes = distinct * gu_e + T * H * 2 + R * I * 4
+    down_bytes = distinct * dn_e + R * I * 4 + T * H * 4
+    step_bytes = distinct * (gu_e + dn_e) + wl.experts * H * 4 + T * H * 2 + T * H * 4
+    flops_gu = 2 * R * 2 * I * H
+    flops_dn = 2 * R * H * I
+    return dict(gateup_bytes=gateup_bytes, down_bytes=down_bytes, step_bytes=step_bytes,
+                gateup_flops=flops_gu, down_flops=flops_dn, step_flops=flops_gu + flops_dn)
+
+
+def cpu_baseline(host_layer, W, n_tokens):
+    import oracle
+
+    wl = W.DECODE
+    x = W.make_x(wl, tokens=n_tokens, stream_offset=999)
+    wr = W.make_router(wl)
+    t0 = time.perf_counter()
+    oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, host_layer, x, wr)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens of the MiMo-shaped MXFP4 layer "
+                      f"(fp32 router, top-8, 8 experts in float64 each), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--layers", type=int, default=4, help="device copies of the layer cycled")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="decode only")
+    ap.add_argument("--only", choices=["decode", "verify", "prefill"], default=None,
+                    help="run one workload without the report (for profilers)")
+    ap.add_argument("--no-peaks", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_moe_gemv_amd as bq
+    import workloads as W
+
+    bq.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    b = Bench(args, torch, bq, W)
+
+    if args.only:
+        wl = {"decode": W.DECODE, "verify": W.VERIFY, "prefill": W.PREFILL}[args.only]
+        res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False)
+        log(json.dumps(res))
+        return
+
+    log("decode T=1")
+    dec = b.run(W.DECODE, args.steps, args.warmup, 1)
+    wl = W.DECODE
+    alg = algorithmic(wl, dec["distinct_experts_last_step"], 1)
+    gu_us = dec["stage_us"]["gateup"]
+    achieved = alg["gateup_bytes"] / (gu_us * 1e-6) / 1e9
+    roof = {"kernel": "decode_gateup_mxfp4", "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": _traffic("decode_gateup_mxfp4", "decode.hip", 1),
+            "algorithmic_bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": gu_us}
+    step_gbs = alg["step_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
+    extra = {"decode_t1": {**dec, "step_algorithmic_bytes": alg["step_bytes"],
+                           "step_hbm_gbs": round(step_gbs, 1),
+                           "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                           "down_hbm_gbs": round(alg["down_bytes"] / (dec["stage_us"]["down"] * 1e-6) / 1e9, 1)}}
+
+    if not args.no_extra:
+        log("verify T=16 (skewed routing)")
+        ver = b.run(W.VERIFY, max(200, args.steps // 4), 50, 16)
+        a = algorithmic(W.VERIFY, ver["distinct_experts_last_step"], 16)
+        extra["verify_t16"] = {**ver, "step_algorithmic_bytes": a["step_bytes"],
+                               "step_hbm_gbs": round(a["step_bytes"] / (ver["ms_per_step"] * 1e-3) / 1e9, 1)}
+        log("prefill T=2048")
+        pre = b.run(W.PREFILL, 30, 5, 2048)
+        a = algorithmic(W.PREFILL, W.PREFILL.experts, 2048)
+        pf = a["step_flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
+        gu_t = a["gateup_flops"] / (pre["stage_us"]["gateup"] * 1e-6) / 1e12
+        dn_t = a["down_flops"] / (pre["stage_us"]["down"] * 1e-6) / 1e12
+        extra["prefill_t2048"] = {
+            **pre, "step_algorithmic_flops": a["step_flops"],
+            "step_mfma_tflops": round(pf, 1), "step_mfma_frac": round(pf / BF16_PEAK_TFLOPS, 4),
+            "step_hbm_frac": round(a["step_bytes"] / (pre["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gateup_mfma_frac": round(gu_t / BF16_PEAK_TFLOPS, 4),
+            "down_mfma_frac": round(dn_t / BF16_PEAK_TFLOPS, 4),
+        }
+    if not args.no_peaks:
+        extra["measured_peaks"] = measured_peaks(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} decode tokens")
+        cpu = cpu_baseline(b.host_layer, W, args.cpu_tokens)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded MXFP4 codes/E8M0 scales, bf16 N(0,1) tokens, fp32 N(0,0.02) router)",
+        "config": {"workload": wl.name, "hidden": wl.hidden, "inter": wl.inter,
+                   "experts": wl.experts, "top_k": wl.top_k, "format": "mxfp4",
+                   "tokens_per_step": 1, "layer_copies": args.layers},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+        "host": {"cpu": platform.processor() or platform.machine(), "gpu": torch.cuda.get_device_name(0)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,8 @@ MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL = 2
 MOE_DECODE_MAX_TOKENS = 16
 
+STAGES = ("router", "select", "permute", "gateup", "down", "combine")
+
 EXPORTED_SYMBOLS = (
     "moe_packed_size",
     "moe_workspace_size",
@@ -37,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "moe_layer_forward",
     "moe_layer_routing",
     "moe_layer_last_path",
+    "moe_layer_set_profiling",
+    "moe_layer_profile_read",
     "moe_layer_destroy",
     "moe_status_str",
 )
@@ -89,6 +93,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_layer_last_path.restype = ctypes.c_int
     lib.moe_layer_destroy.argtypes = [P]
     lib.moe_layer_destroy.restype = None
+    lib.moe_layer_set_profiling.argtypes = [P, ctypes.c_int32]
+    lib.moe_layer_set_profiling.restype = ctypes.c_int
+    lib.moe_layer_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]
+    lib.moe_layer_profile_read.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -214,6 +222,29 @@ class MoeLayer:
         if rc != MOE_OK:
             raise MoeError(rc, "moe_layer_routing")
         return r
+
+    def set_profiling(self, slots: int):
+        """Record per-stage HIP event pairs for the next forwards (round robin
+        over `slots`); 0 turns it off."""
+        rc = self._lib.moe_layer_set_profiling(self._handle, slots)
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layer_set_profiling")
+        self._prof_slots = slots
+
+    def profile_read(self):
+        """Per-stage kernel milliseconds, a list (per slot) of dicts keyed by
+        stage name; stages that did not run are absent."""
+        n = getattr(self, "_prof_slots", 0)
+        buf = (ctypes.c_float * (n * len(STAGES)))()
+        rc = self._lib.moe_layer_profile_read(self._handle, buf, n)
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_layer_profile_read")
+        out = []
+        for s in range(n):
+            row = {STAGES[i]: buf[s * len(STAGES) + i] for i in range(len(STAGES))
+                   if buf[s * len(STAGES) + i] >= 0}
+            out.append(row)
+        return out
 
     def last_path(self) -> int:
         return self._lib.moe_layer_last_path(self._handle)

@@ -1,6 +1,7 @@
 // abi.cpp -- the exported C entry points of libbqmoe.so: argument validation,
 // workspace carving and the launch sequence of one forward pass.
 #include <new>
+#include <vector>
 
 #include "../../include/bqmoe.h"
 #include "moe_internal.h"
@@ -15,7 +16,34 @@ struct moe_layer {
     Workspace ws;
     int last_T;
     int last_path;
+    bool arrivals_ready;  // the router's arrival counter has been zeroed on the device
+    // per-stage timing (moe_layer_set_profiling)
+    int prof_slots;
+    int prof_next;
+    std::vector<hipEvent_t> prof_ev;  // [slots][MOE_N_STAGES][2]
+    std::vector<char> prof_ran;       // [slots][MOE_N_STAGES]
 };
+
+static void prof_release(moe_layer *L) {
+    for (hipEvent_t e : L->prof_ev)
+        if (e) (void)hipEventDestroy(e);
+    L->prof_ev.clear();
+    L->prof_ran.clear();
+    L->prof_slots = 0;
+    L->prof_next = 0;
+}
+
+// Runs one launcher, bracketed by the slot's event pair when profiling.
+template <class F>
+static hipError_t staged(moe_layer *L, int slot, int stage, hipStream_t st, F &&launch) {
+    if (slot < 0) return launch();
+    hipEvent_t *ev = &L->prof_ev[((size_t)slot * MOE_N_STAGES + stage) * 2];
+    hipError_t e = hipEventRecord(ev[0], st);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = hipEventRecord(ev[1], st);
+    if (e == hipSuccess) L->prof_ran[(size_t)slot * MOE_N_STAGES + stage] = 1;
+    return e;
+}
 
 namespace bqmoe {
 
@@ -32,7 +60,7 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256((size_t)(s.E + 1) * 4);   // active
     b += align256(R * 4);                   // perm
     b += align256(R * 4);                   // inv
-    b += align256((size_t)(s.H / 16) * 4);  // sync
+    b += align256(4);                       // arrivals
     b += align256(R * s.I * 4);             // h
     b += align256(R * s.H * 4);             // y
     return b;
@@ -54,7 +82,7 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->active = reinterpret_cast<int32_t *>(take((size_t)(s.E + 1) * 4));
     ws->perm = reinterpret_cast<int32_t *>(take(R * 4));
     ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
-    ws->sync = reinterpret_cast<uint32_t *>(take((size_t)(s.H / 16) * 4));
+    ws->arrivals = reinterpret_cast<uint32_t *>(take(4));
     ws->h = take(R * s.I * 4);
     ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
 }
@@ -77,9 +105,6 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
     } else {
         return MOE_EINVAL;
     }
-    // decode kernels hold one wave's packed bytes in registers
-    if (d->force_path != MOE_PATH_PREFILL && (d->hidden > 8192 || d->inter > 2048))
-        return MOE_EUNSUPPORTED;
     if (s) {
         s->H = d->hidden;
         s->I = d->inter;
@@ -95,6 +120,8 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
             s->books_bytes = kVqBooksBytes;
         }
     }
+    // the decode kernels are instantiated for power-of-two widths
+    if (d->force_path == MOE_PATH_DECODE && s && !decode_supported(*s)) return MOE_EUNSUPPORTED;
     return MOE_OK;
 }
 
@@ -138,6 +165,9 @@ int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_byte
     carve_workspace(s, desc->max_tokens, workspace, &L->ws);
     L->last_T = 0;
     L->last_path = MOE_EINVAL;
+    L->arrivals_ready = false;
+    L->prof_slots = 0;
+    L->prof_next = 0;
     *out = L;
     return MOE_OK;
 }
@@ -150,7 +180,9 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
         !aligned16(out))
         return MOE_EINVAL;
     int path = L->desc.force_path;
-    if (path == MOE_PATH_AUTO) path = (T <= kDecodeMaxTokens) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_AUTO)
+        path = (T <= kDecodeMaxTokens && decode_supported(L->shape)) ? MOE_PATH_DECODE
+                                                                     : MOE_PATH_PREFILL;
     if (path == MOE_PATH_DECODE && T > kDecodeMaxTokens) return MOE_EINVAL;
     const Shape &s = L->shape;
     const Workspace &ws = L->ws;
@@ -158,17 +190,44 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
     const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
     const uint8_t *packed = static_cast<const uint8_t *>(packed_experts);
 
-    hipError_t err = launch_router(s, x, router_w, T, ws.logits, st);
+    int slot = -1;
+    if (L->prof_slots > 0) {
+        slot = L->prof_next;
+        L->prof_next = (L->prof_next + 1) % L->prof_slots;
+        for (int i = 0; i < MOE_N_STAGES; ++i) L->prof_ran[(size_t)slot * MOE_N_STAGES + i] = 0;
+    }
+    hipError_t err = hipSuccess;
     if (path == MOE_PATH_DECODE) {
-        if (err == hipSuccess) err = launch_route_small(s, T, ws, st);
-        if (err == hipSuccess) err = launch_decode_gateup(s, T, x, packed, ws, st);
-        if (err == hipSuccess) err = launch_decode_down(s, T, packed, ws, out, st);
+        if (!L->arrivals_ready) {
+            // once per handle: the counter then resets itself at the end of every call
+            err = launch_zero_arrivals(ws, st);
+            if (err == hipSuccess) L->arrivals_ready = true;
+        }
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_ROUTER, st,
+                         [&] { return launch_router_route_small(s, x, router_w, T, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_GATEUP, st,
+                         [&] { return launch_decode_gateup(s, T, x, packed, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_DOWN, st,
+                         [&] { return launch_decode_down(s, T, packed, ws, out, st); });
     } else {
-        if (err == hipSuccess) err = launch_topk(s, T, ws, st);
-        if (err == hipSuccess) err = launch_permute(s, T, ws, st);
-        if (err == hipSuccess) err = launch_prefill_gateup(s, T, x, packed, ws, st);
-        if (err == hipSuccess) err = launch_prefill_down(s, T, packed, ws, st);
-        if (err == hipSuccess) err = launch_combine(s, T, ws, out, st);
+        err = staged(L, slot, MOE_STAGE_ROUTER, st,
+                     [&] { return launch_router(s, x, router_w, T, ws.logits, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_PERMUTE, st, [&] { return launch_permute(s, T, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_GATEUP, st,
+                         [&] { return launch_prefill_gateup(s, T, x, packed, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_DOWN, st,
+                         [&] { return launch_prefill_down(s, T, packed, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_COMBINE, st,
+                         [&] { return launch_combine(s, T, ws, out, st); });
     }
     if (err != hipSuccess) return MOE_EHIP;
     L->last_T = T;
@@ -197,7 +256,45 @@ int moe_layer_routing(moe_layer *L, int32_t *topk_idx, float *topk_w, int32_t *c
 
 int moe_layer_last_path(const moe_layer *L) { return L && L->last_T > 0 ? L->last_path : MOE_EINVAL; }
 
-void moe_layer_destroy(moe_layer *L) { delete L; }
+int moe_layer_set_profiling(moe_layer *L, int32_t slots) {
+    if (!L || slots < 0 || slots > 65536) return MOE_EINVAL;
+    prof_release(L);
+    if (slots == 0) return MOE_OK;
+    L->prof_ev.assign((size_t)slots * MOE_N_STAGES * 2, nullptr);
+    L->prof_ran.assign((size_t)slots * MOE_N_STAGES, 0);
+    for (hipEvent_t &e : L->prof_ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            prof_release(L);
+            return MOE_EHIP;
+        }
+    }
+    L->prof_slots = slots;
+    L->prof_next = 0;
+    return MOE_OK;
+}
+
+int moe_layer_profile_read(moe_layer *L, float *ms, int32_t slots) {
+    if (!L || !ms || slots != L->prof_slots || slots <= 0) return MOE_EINVAL;
+    for (int sl = 0; sl < slots; ++sl)
+        for (int st = 0; st < MOE_N_STAGES; ++st) {
+            const size_t i = (size_t)sl * MOE_N_STAGES + st;
+            ms[i] = -1.0f;
+            if (!L->prof_ran[i]) continue;
+            hipEvent_t *ev = &L->prof_ev[i * 2];
+            if (hipEventSynchronize(ev[1]) != hipSuccess) return MOE_EHIP;
+            float t = 0.0f;
+            if (hipEventElapsedTime(&t, ev[0], ev[1]) != hipSuccess) return MOE_EHIP;
+            ms[i] = t;
+        }
+    return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer *L) {
+    if (!L) return;
+    prof_release(L);
+    delete L;
+}
 
 const char *moe_status_str(int status) {
     switch (status) {

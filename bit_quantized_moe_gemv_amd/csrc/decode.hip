@@ -43,21 +43,41 @@ __device__ __forceinline__ void fp4x32_to_f32(const uint4 v, float scale, f32x2 
     }
 }
 
+constexpr int kRing = 4;  // 1 KiB wave loads kept in flight per wave
+
+// Global loads below never sit under a divergent branch: predicated loads make
+// the compiler fall back to waiting for every outstanding load at the branch
+// joins, which serialises the weight stream.  Shapes are template parameters
+// and out-of-range staging loads are clamped duplicates instead of skipped.
+__device__ __forceinline__ uint4 ld16(const uint8_t *base, uint32_t off) {
+    return *reinterpret_cast<const uint4 *>(base + off);
+}
+
+// Empty asm register fences: the value becomes opaque at this point of the
+// program, so the compiler can neither hoist its consumers above it (e.g. all
+// conversions above the staging barrier) nor sink it.  Used to keep the ring's
+// per-super-step order and register footprint.
+__device__ __forceinline__ void reg_fence(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void reg_fence(uint4 &v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Grid: (expert slots, I/16).  Block: 4 waves; the block
-// owns 16 gate rows and the matching 16 up rows of one active expert, the
-// waves split the K super-steps (J = wave, wave+4, ...).  Each wave loads all
-// of its packed bytes up front (MAXJ super-steps), then sweeps the expert's
-// routes kDecTC at a time with x staged in LDS.  h is written in fp32, in
-// route-position order: h[p][i].
+// gate/up + SwiGLU.  Grid: (expert slots, I/16).  Block: 4 waves owning the
+// 16 gate rows and the 16 matching up rows of one row group of one active
+// expert: wave w streams matrix w/2 (gate, up) over K half w%2, a contiguous
+// run of NJ = H/256 super-steps of 1 KiB, with kRing loads in flight.  The x
+// rows of up to TC routes are fetched first and staged in LDS behind an
+// LDS-only barrier, so the weight stream is never stalled by them.  h is
+// written in fp32, in route-position order.
 // ---------------------------------------------------------------------------
-template <int MAXJ>
+template <int NJ, int TC>
 __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
     int H, int I, int K, const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, float *__restrict__ h) {
-    extern __shared__ __align__(16) uint16_t xs[];  // [kDecTC][H]
-    __shared__ float red[4][kDecTC][16][2];
+    extern __shared__ __align__(16) uint16_t xs[];  // [TC][H]
+    __shared__ float red[4][TC][16];
     const int slot = blockIdx.x;
     if (slot >= active[0]) return;
     const int e = active[1 + slot];
@@ -66,243 +86,286 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const int rg = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, q = lane >> 4;
+    const int mat = wave >> 1, kh = wave & 1;
 
-    const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const size_t kt = (size_t)(H / 32);  // tiles along K per row group
-    const uint8_t *gcode = ex + (size_t)rg * kt * 256;
-    const uint8_t *ucode = ex + (size_t)(I / 16 + rg) * kt * 256;
-    const uint8_t *scl = ex + (size_t)I * H;  // gate/up scale region
-    const uint8_t *gscl = scl + (size_t)rg * kt * 16;
-    const uint8_t *uscl = scl + (size_t)(I / 16 + rg) * kt * 16;
-    const int nsuper = H / 128;
+    const size_t grp = (size_t)(mat ? I / 16 + rg : rg);
+    const uint8_t *ex = packed + (size_t)e * expert_bytes;
+    const uint8_t *cbase = ex + (grp * kt + (size_t)kh * NJ * 4) * 256;          // wave's first tile
+    const uint8_t *sbase = ex + (size_t)I * H + (grp * kt + (size_t)kh * NJ * 4) * 16;
+    const uint32_t coff = (uint32_t)(q * 256 + n * 16);
+    const uint32_t soff = (uint32_t)(q * 16 + n);
+    const int per_row = H / 8;                   // uint4 per x row
+    constexpr int XN = (TC * NJ * 32 + 255) / 256;  // uint4 per thread for TC rows (H = 256*NJ)
 
-    uint4 gv[MAXJ], uv[MAXJ];
-    uint32_t gs[MAXJ], us[MAXJ];
+    for (int c0 = 0; c0 < ne; c0 += TC) {
+        const int nt = min(TC, ne - c0);
+        if (c0 > 0) lds_barrier();  // previous chunk's readers are done with xs and red
+        // token of each staged row: uniform values, read through the scalar unit
+        // so that they do not queue behind the vector loads
+        int trow[TC];
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-        const int J = wave + 4 * j;
-        if (J < nsuper) {
-            const size_t tile = (size_t)(4 * J + q);
-            gv[j] = *reinterpret_cast<const uint4 *>(gcode + tile * 256 + n * 16);
-            uv[j] = *reinterpret_cast<const uint4 *>(ucode + tile * 256 + n * 16);
-            gs[j] = gscl[tile * 16 + n];
-            us[j] = uscl[tile * 16 + n];
+        for (int r = 0; r < TC; ++r) trow[r] = perm[p0 + c0 + min(r, nt - 1)] / K;
+        uint4 xv[XN];
+#pragma unroll
+        for (int i = 0; i < XN; ++i) {
+            const int idx = min(tid + 256 * i, TC * per_row - 1);
+            const int r = idx / per_row, c = idx - r * per_row;
+            int t = trow[0];
+#pragma unroll
+            for (int rr = 1; rr < TC; ++rr) t = (r == rr) ? trow[rr] : t;
+            xv[i] = reinterpret_cast<const uint4 *>(x + (size_t)t * H)[c];
         }
-    }
+        __builtin_amdgcn_sched_barrier(0);  // x loads first, then the weight ring
+        uint4 ring[kRing];
+        uint32_t sring[kRing];
+#pragma unroll
+        for (int j = 0; j < kRing && j < NJ; ++j) {
+            ring[j] = ld16(cbase, coff + j * 1024);
+            sring[j] = sbase[soff + j * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < XN; ++i)
+            reinterpret_cast<uint4 *>(xs)[min(tid + 256 * i, TC * per_row - 1)] = xv[i];
+        lds_barrier();
 
-    for (int c0 = 0; c0 < ne; c0 += kDecTC) {
-        const int nt = min(kDecTC, ne - c0);
-        __syncthreads();
-        const int per_row = H / 8;  // uint4 per x row
-        for (int i = tid; i < nt * per_row; i += 256) {
-            const int r = i / per_row, c = i - r * per_row;
-            const int t = perm[p0 + c0 + r] / K;
-            reinterpret_cast<uint4 *>(xs)[r * per_row + c] =
-                reinterpret_cast<const uint4 *>(x + (size_t)t * H)[c];
-        }
-        __syncthreads();
-        float ga[kDecTC], ua[kDecTC];
+        float acc[TC];
 #pragma unroll
-        for (int tt = 0; tt < kDecTC; ++tt) { ga[tt] = 0.f; ua[tt] = 0.f; }
+        for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
 #pragma unroll
-        for (int j = 0; j < MAXJ; ++j) {
-            const int J = wave + 4 * j;
-            if (J < nsuper) {
-                bf16x2 gw[16], uw[16];
-                fp4x32_to_bf16(gv[j], e8m0_to_f32(gs[j]), gw);
-                fp4x32_to_bf16(uv[j], e8m0_to_f32(us[j]), uw);
+        for (int j = 0; j < NJ; ++j) {
+            uint4 wv = ring[j % kRing];
+            uint32_t sv = sring[j % kRing];
+            reg_fence(wv);
+            reg_fence(sv);
+            const float sc = e8m0_to_f32(sv);
+            if (j + kRing < NJ) {
+                uint32_t o = coff + (j + kRing) * 1024, so = soff + (j + kRing) * 64;
+                reg_fence(o);
+                reg_fence(so);
+                ring[j % kRing] = ld16(cbase, o);
+                sring[j % kRing] = sbase[so];
+            }
+            bf16x2 w2[16];
+            fp4x32_to_bf16(wv, sc, w2);
+            const int J = kh * NJ + j;
 #pragma unroll
-                for (int tt = 0; tt < kDecTC; ++tt) {
-                    if (tt < nt) {
-                        const uint4 *xr =
-                            reinterpret_cast<const uint4 *>(xs + tt * H + 128 * J + 32 * q);
-                        union { uint4 u[4]; bf16x2 p[16]; } xv;
+            for (int tt = 0; tt < TC; ++tt) {
+                if (tt < nt) {
+                    const uint4 *xr = reinterpret_cast<const uint4 *>(xs + tt * H + 128 * J + 32 * q);
+                    union { uint4 u[4]; bf16x2 p[16]; } xx;
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) xv.u[m] = xr[m];
-                        float g = ga[tt], u = ua[tt];
+                    for (int m = 0; m < 4; ++m) xx.u[m] = xr[m];
+                    float a = acc[tt];
 #pragma unroll
-                        for (int b = 0; b < 16; ++b) {
-                            g = __builtin_amdgcn_fdot2_f32_bf16(gw[b], xv.p[b], g, false);
-                            u = __builtin_amdgcn_fdot2_f32_bf16(uw[b], xv.p[b], u, false);
-                        }
-                        ga[tt] = g;
-                        ua[tt] = u;
-                    }
+                    for (int b = 0; b < 16; ++b)
+                        a = __builtin_amdgcn_fdot2_f32_bf16(w2[b], xx.p[b], a, false);
+                    acc[tt] = a;
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int tt = 0; tt < kDecTC; ++tt) {
-            ga[tt] += __shfl_xor(ga[tt], 16, 64);
-            ga[tt] += __shfl_xor(ga[tt], 32, 64);
-            ua[tt] += __shfl_xor(ua[tt], 16, 64);
-            ua[tt] += __shfl_xor(ua[tt], 32, 64);
-            if (q == 0) {
-                red[wave][tt][n][0] = ga[tt];
-                red[wave][tt][n][1] = ua[tt];
-            }
+        for (int tt = 0; tt < TC; ++tt) {
+            acc[tt] += __shfl_xor(acc[tt], 16, 64);
+            acc[tt] += __shfl_xor(acc[tt], 32, 64);
+            if (q == 0) red[wave][tt][n] = acc[tt];
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < nt * 16) {
             const int tt = tid >> 4, nn = tid & 15;
-            const float g = ((red[0][tt][nn][0] + red[1][tt][nn][0]) + red[2][tt][nn][0]) + red[3][tt][nn][0];
-            const float u = ((red[0][tt][nn][1] + red[1][tt][nn][1]) + red[2][tt][nn][1]) + red[3][tt][nn][1];
+            const float g = red[0][tt][nn] + red[1][tt][nn];
+            const float u = red[2][tt][nn] + red[3][tt][nn];
             h[(size_t)(p0 + c0 + tt) * I + 16 * rg + nn] = silu_f32(g) * u;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// down projection + weighted combine.  Grid: (expert slots, H/64).  Block: 4
-// waves, wave w owns output row group 4*blockIdx.y + w (16 rows) and sweeps all
-// I/128 super-steps itself.  y[p][j] is written per route position; the last
-// block to finish a 64-row block (counted with a device-scope atomic) forms
-// out[t][j] = sum_s w[t,s] * y[inv[t,s]][j] in slot order, so the result does
-// not depend on block timing.
+// down projection + weighted combine.  Grid: H/16 blocks (one 16-row group of
+// the output each) of 16 waves.  The block covers every active expert: wave w
+// takes active slots w/2, w/2+8, ... and K half w%2 of their 16 down rows
+// (NJ = I/256 super-steps; with I = 128 the second half is empty).  Per slot
+// it fetches its half of the route's h row into its own LDS area, then its
+// packed bytes (kept in registers while the expert's further routes are
+// processed), computing each super-step as it arrives.  Route outputs
+// y[p][16] (two K halves) stay in LDS; after one barrier the block forms
+// out[t][j] = sum_s w[t,s] * y[inv[t,s]][j] in slot order.  No atomics and no
+// cross-block traffic: the result is bitwise reproducible.
 // ---------------------------------------------------------------------------
-template <int MAXJ>
-__global__ __launch_bounds__(256) void decode_down_mxfp4(
+constexpr int kDnWaves = 16;
+constexpr int kDnMaxI = 2048;
+constexpr int kDnMaxR = kDecodeMaxTokens * kMaxTopK;
+
+template <int NJ>
+__global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int T,
     const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
-    const float *__restrict__ h, float *__restrict__ y, const float *__restrict__ wts,
-    const int32_t *__restrict__ inv, uint32_t *__restrict__ sync, float *__restrict__ out) {
-    extern __shared__ __align__(16) float hs[];  // [kDecTC][I]
-    __shared__ int s_last;
-    const int slot = blockIdx.x;
-    const int n_active = active[0];
-    if (slot >= n_active) return;
-    const int e = active[1 + slot];
-    const int p0 = offsets[e];
-    const int ne = offsets[e + 1] - p0;
+    const float *__restrict__ h, const float *__restrict__ wts, const int32_t *__restrict__ inv,
+    float *__restrict__ out) {
+    __shared__ __align__(16) float hs[kDnWaves][kDnMaxI / 2];
+    __shared__ float ys[2][kDnMaxR][16];
+    __shared__ float s_w[kDnMaxR];
+    __shared__ int s_inv[kDnMaxR];
+    const int a = blockIdx.x;  // output row group
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, q = lane >> 4;
-    const int a = blockIdx.y * 4 + wave;  // output row group
-
-    const uint8_t *ex = packed + (size_t)e * expert_bytes;
-    const uint8_t *dcode = ex + (size_t)I * H + (size_t)I * H / 16;
-    const uint8_t *dscl = dcode + (size_t)H * I / 2;
+    const int kh = wave & 1;
+    const int n_active = active[0];
+    const int R = T * K;
+    // routing weights of the combine, fetched now so their latency is hidden
+    const int rr = min(tid, R - 1);
+    const float my_w = wts[rr];
+    const int my_inv = inv[rr];
+    const bool live = kh * NJ * 128 < I;  // false only for the empty second half when I = 128
     const size_t kt = (size_t)(I / 32);
-    const int nsuper = I / 128;
+    const uint32_t coff = (uint32_t)(q * 256 + n * 16);
+    const uint32_t soff = (uint32_t)(q * 16 + n);
+    float *hw = hs[wave];
 
-    uint4 cv[MAXJ];
-    uint32_t cs[MAXJ];
-#pragma unroll
-    for (int J = 0; J < MAXJ; ++J) {
-        if (J < nsuper) {
-            const size_t tile = (size_t)a * kt + 4 * J + q;
-            cv[J] = *reinterpret_cast<const uint4 *>(dcode + tile * 256 + n * 16);
-            cs[J] = dscl[tile * 16 + n];
+    for (int qs = wave >> 1; qs < n_active; qs += kDnWaves / 2) {
+        const int e = active[1 + qs];
+        const int p0 = offsets[e];
+        const int ne = offsets[e + 1] - p0;
+        if (!live) {
+            for (int r = 0; r < ne; ++r)
+                if (q == 0) ys[kh][p0 + r][n] = 0.f;
+            continue;
         }
-    }
+        const uint8_t *ex = packed + (size_t)e * expert_bytes;
+        const uint8_t *dcode = ex + (size_t)I * H + (size_t)I * H / 16;
+        const uint8_t *dscl = dcode + (size_t)H * I / 2;
+        const uint8_t *cbase = dcode + ((size_t)a * kt + (size_t)kh * NJ * 4) * 256;
+        const uint8_t *sbase = dscl + ((size_t)a * kt + (size_t)kh * NJ * 4) * 16;
 
-    for (int c0 = 0; c0 < ne; c0 += kDecTC) {
-        const int nt = min(kDecTC, ne - c0);
-        __syncthreads();
-        const int per_row = I / 4;  // float4 per h row
-        for (int i = tid; i < nt * per_row; i += 256)
-            reinterpret_cast<float4 *>(hs)[i] =
-                reinterpret_cast<const float4 *>(h + (size_t)(p0 + c0) * I)[i];
-        __syncthreads();
-        float acc[kDecTC];
+        uint4 cv[NJ];
+        uint32_t cs[NJ];
+        for (int r = 0; r < ne; ++r) {
+            // this wave's half of h[p]: floats [128*NJ*kh, 128*NJ*(kh+1)), two per lane per step
+            const float2 *hrow =
+                reinterpret_cast<const float2 *>(h + (size_t)(p0 + r) * I + 128 * NJ * kh);
+            float2 hv[NJ];
 #pragma unroll
-        for (int tt = 0; tt < kDecTC; ++tt) acc[tt] = 0.f;
+            for (int j = 0; j < NJ; ++j) hv[j] = hrow[64 * j + lane];
+            if (r == 0) {
 #pragma unroll
-        for (int J = 0; J < MAXJ; ++J) {
-            if (J < nsuper) {
-                f32x2 wv[16];
-                fp4x32_to_f32(cv[J], e8m0_to_f32(cs[J]), wv);
-#pragma unroll
-                for (int tt = 0; tt < kDecTC; ++tt) {
-                    if (tt < nt) {
-                        const float4 *hr =
-                            reinterpret_cast<const float4 *>(hs + tt * I + 128 * J + 32 * q);
-                        float s = acc[tt];
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            const float4 hv = hr[m];
-                            s = __builtin_fmaf(wv[2 * m].x, hv.x, s);
-                            s = __builtin_fmaf(wv[2 * m].y, hv.y, s);
-                            s = __builtin_fmaf(wv[2 * m + 1].x, hv.z, s);
-                            s = __builtin_fmaf(wv[2 * m + 1].y, hv.w, s);
-                        }
-                        acc[tt] = s;
-                    }
+                for (int j = 0; j < NJ; ++j) {
+                    cv[j] = ld16(cbase, coff + j * 1024);
+                    cs[j] = sbase[soff + j * 64];
                 }
             }
-        }
 #pragma unroll
-        for (int tt = 0; tt < kDecTC; ++tt) {
-            acc[tt] += __shfl_xor(acc[tt], 16, 64);
-            acc[tt] += __shfl_xor(acc[tt], 32, 64);
-            if (q == 0 && tt < nt) y[(size_t)(p0 + c0 + tt) * H + 16 * a + n] = acc[tt];
+            for (int j = 0; j < NJ; ++j) reinterpret_cast<float2 *>(hw)[64 * j + lane] = hv[j];
+            lds_wave_sync();
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                uint4 wv = cv[j];
+                uint32_t sv = cs[j];
+                reg_fence(wv);
+                reg_fence(sv);
+                const float sc = e8m0_to_f32(sv);
+                const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+                const float4 *hr = reinterpret_cast<const float4 *>(hw + 128 * j + 32 * q);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], sc, 0);
+                    const f32x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], sc, 1);
+                    const f32x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], sc, 2);
+                    const f32x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], sc, 3);
+                    const float4 v0 = hr[2 * i], v1 = hr[2 * i + 1];
+                    acc = __builtin_fmaf(w0.x, v0.x, acc);
+                    acc = __builtin_fmaf(w0.y, v0.y, acc);
+                    acc = __builtin_fmaf(w1.x, v0.z, acc);
+                    acc = __builtin_fmaf(w1.y, v0.w, acc);
+                    acc = __builtin_fmaf(w2.x, v1.x, acc);
+                    acc = __builtin_fmaf(w2.y, v1.y, acc);
+                    acc = __builtin_fmaf(w3.x, v1.z, acc);
+                    acc = __builtin_fmaf(w3.y, v1.w, acc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            acc += __shfl_xor(acc, 16, 64);
+            acc += __shfl_xor(acc, 32, 64);
+            if (q == 0) ys[kh][p0 + r][n] = acc;
+            lds_wave_sync();
         }
     }
-
-    // publish y, then count arrivals for this 64-row block
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&sync[blockIdx.y], 1u);
-        s_last = (prev == (uint32_t)(n_active - 1));
+    if (tid < R) {
+        s_w[tid] = my_w;
+        s_inv[tid] = my_inv;
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int j0 = blockIdx.y * 64;
-    for (int i = tid; i < T * 64; i += 256) {
-        const int t = i >> 6, j = j0 + (i & 63);
+    lds_barrier();
+    for (int i = tid; i < T * 16; i += kDnWaves * 64) {
+        const int t = i >> 4, nn = i & 15;
         float acc = 0.f;
-        for (int s = 0; s < K; ++s)
-            acc = __builtin_fmaf(wts[t * K + s], y[(size_t)inv[t * K + s] * H + j], acc);
-        out[(size_t)t * H + j] = acc;
+        for (int s = 0; s < K; ++s) {
+            const int p = s_inv[t * K + s];
+            acc = __builtin_fmaf(s_w[t * K + s], ys[0][p][nn] + ys[1][p][nn], acc);
+        }
+        out[(size_t)t * H + 16 * a + nn] = acc;
     }
 }
 
-template <int MAXJ>
+template <int NJ, int TC>
 static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
     const int slots = min(s.E, T * s.K);
     dim3 grid(slots, s.I / 16);
-    const size_t lds = (size_t)kDecTC * s.H * 2;
-    decode_gateup_mxfp4<MAXJ><<<grid, 256, lds, st>>>(x, packed, s.expert_bytes, s.H, s.I, s.K,
-                                                      ws.active, ws.offsets, ws.perm,
-                                                      static_cast<float *>(ws.h));
+    decode_gateup_mxfp4<NJ, TC><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
+        x, packed, s.expert_bytes, s.H, s.I, s.K, ws.active, ws.offsets, ws.perm,
+        static_cast<float *>(ws.h));
     return hipGetLastError();
+}
+
+template <int NJ>
+static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
+                                   const uint8_t *packed, const Workspace &ws, hipStream_t st) {
+    return T == 1 ? gateup_launch<NJ, 1>(s, T, x, packed, ws, st)
+                  : gateup_launch<NJ, kDecTC>(s, T, x, packed, ws, st);
+}
+
+bool decode_supported(const Shape &s) {
+    const int nj = s.H / 256;
+    const bool h_ok = nj == 1 || nj == 2 || nj == 4 || nj == 8 || nj == 16 || nj == 32;
+    const bool i_ok = s.I == 128 || s.I == 256 || s.I == 512 || s.I == 1024 || s.I == 2048;
+    return h_ok && i_ok;
 }
 
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
-    const int per_wave = (s.H / 128 + 3) / 4;
-    if (per_wave <= 1) return gateup_launch<1>(s, T, x, packed, ws, st);
-    if (per_wave <= 2) return gateup_launch<2>(s, T, x, packed, ws, st);
-    if (per_wave <= 4) return gateup_launch<4>(s, T, x, packed, ws, st);
-    if (per_wave <= 8) return gateup_launch<8>(s, T, x, packed, ws, st);
-    if (per_wave <= 16) return gateup_launch<16>(s, T, x, packed, ws, st);
-    return hipErrorInvalidValue;
+    switch (s.H / 256) {
+        case 1: return gateup_launch_tc<1>(s, T, x, packed, ws, st);
+        case 2: return gateup_launch_tc<2>(s, T, x, packed, ws, st);
+        case 4: return gateup_launch_tc<4>(s, T, x, packed, ws, st);
+        case 8: return gateup_launch_tc<8>(s, T, x, packed, ws, st);
+        case 16: return gateup_launch_tc<16>(s, T, x, packed, ws, st);
+        case 32: return gateup_launch_tc<32>(s, T, x, packed, ws, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-template <int MAXJ>
+template <int NJ>
 static hipError_t down_launch(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                               float *out, hipStream_t st) {
-    const int slots = min(s.E, T * s.K);
-    dim3 grid(slots, s.H / 64);
-    const size_t lds = (size_t)kDecTC * s.I * 4;
-    decode_down_mxfp4<MAXJ><<<grid, 256, lds, st>>>(packed, s.expert_bytes, s.H, s.I, s.K, T,
-                                                    ws.active, ws.offsets,
-                                                    static_cast<const float *>(ws.h), ws.y, ws.w,
-                                                    ws.inv, ws.sync, out);
+    decode_down_mxfp4<NJ><<<s.H / 16, kDnWaves * 64, 0, st>>>(
+        packed, s.expert_bytes, s.H, s.I, s.K, T, ws.active, ws.offsets,
+        static_cast<const float *>(ws.h), ws.w, ws.inv, out);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                               float *out, hipStream_t st) {
-    const int nsuper = s.I / 128;
-    if (nsuper <= 1) return down_launch<1>(s, T, packed, ws, out, st);
-    if (nsuper <= 2) return down_launch<2>(s, T, packed, ws, out, st);
-    if (nsuper <= 4) return down_launch<4>(s, T, packed, ws, out, st);
-    if (nsuper <= 8) return down_launch<8>(s, T, packed, ws, out, st);
-    if (nsuper <= 16) return down_launch<16>(s, T, packed, ws, out, st);
-    return hipErrorInvalidValue;
+    if (s.I > kDnMaxI || T * s.K > kDnMaxR) return hipErrorInvalidValue;
+    switch (s.I) {
+        case 128:
+        case 256: return down_launch<1>(s, T, packed, ws, out, st);
+        case 512: return down_launch<2>(s, T, packed, ws, out, st);
+        case 1024: return down_launch<4>(s, T, packed, ws, out, st);
+        case 2048: return down_launch<8>(s, T, packed, ws, out, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bqmoe

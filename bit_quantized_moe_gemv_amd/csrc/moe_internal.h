@@ -39,7 +39,7 @@ struct Workspace {
     int32_t *active;   // [1 + E]: n_active, then active experts ascending
     int32_t *perm;     // [Rmax]
     int32_t *inv;      // [Rmax]
-    uint32_t *sync;    // [H/16] arrival counters of the decode combine
+    uint32_t *arrivals;  // [1] block arrival counter of the small-batch router
     void *h;           // [Rmax][I] fp32 (decode) or two [Rmax][I] bf16 arrays (prefill)
     float *y;          // [Rmax][H] fp32 per-route expert outputs
 };
@@ -50,9 +50,12 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws);
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
                          hipStream_t st);
-hipError_t launch_route_small(const Shape &s, int T, const Workspace &ws, hipStream_t st);
+hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
+                                     const Workspace &ws, hipStream_t st);
+hipError_t launch_zero_arrivals(const Workspace &ws, hipStream_t st);
 hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_t st);
+bool decode_supported(const Shape &s);
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st);
 hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
@@ -86,6 +89,62 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t v, float scale) {
     r.v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 2);
     r.v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 3);
     return r.v8;
+}
+
+// Workgroup barrier that orders LDS only.  Unlike __syncthreads() it does not
+// wait for outstanding global loads, so weight streams stay in flight across
+// it.  Use only where the barrier protects LDS data.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders one wave's own LDS writes before its later LDS reads.
+__device__ __forceinline__ void lds_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// DPP lane moves (gfx9 encodings).
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// v from lane (per CTRL), or `old` where the lane has no source / is masked.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_or_old(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Exact wave-wide maximum of a float (returned to every lane).  Lane i of each
+// row takes the max of lanes i-1, i-2, i-4, i-8 (so lane 15 holds its row's
+// max), then row broadcasts carry rows 0..3 into lane 63.  Max is exact and
+// order-free, so this equals any other reduction order.
+__device__ __forceinline__ float wave_max_f32(float v) {
+    int b = __float_as_int(v);
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowShr1>(b, b))));
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowShr2>(b, b))));
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowShr4>(b, b))));
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowShr8>(b, b))));
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowBcast15, 0xA>(b, b))));
+    b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_or_old<kDppRowBcast31, 0xC>(b, b))));
+    return __int_as_float(__builtin_amdgcn_readlane(b, 63));
+}
+
+// Wave-wide minimum of an int (returned to every lane); same lane pattern.
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, dpp_or_old<kDppRowShr1>(v, v));
+    v = min(v, dpp_or_old<kDppRowShr2>(v, v));
+    v = min(v, dpp_or_old<kDppRowShr4>(v, v));
+    v = min(v, dpp_or_old<kDppRowShr8>(v, v));
+    v = min(v, dpp_or_old<kDppRowBcast15, 0xA>(v, v));
+    v = min(v, dpp_or_old<kDppRowBcast31, 0xC>(v, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float wave_sum_xor(float v, int from_mask) {

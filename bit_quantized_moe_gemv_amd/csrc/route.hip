@@ -14,6 +14,87 @@
 namespace bqmoe {
 
 // ---------------------------------------------------------------------------
+// top-k of one token by one wave
+// ---------------------------------------------------------------------------
+
+// (value, index) key: a beats b if its value is larger, or equal with a lower
+// index.  Comparing floats makes -0 and +0 equal, so they tie to the index.
+__device__ __forceinline__ bool key_beats(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Selects the k best experts of `l` (E <= 256 logits) and their softmax
+// weights.  Every lane returns the same idx[]/w[]; lane l owns experts l,
+// l+64, l+128, l+192, sorted once by key.  Each round reduces the lanes' heads
+// to the wave maximum, then to the lowest expert index holding it (both
+// reductions are exact, so the winner does not depend on reduction order); the
+// winning lane pops its head.
+__device__ __forceinline__ void cswap(float &va, int &ia, float &vb, int &ib) {
+    // after the call (va, ia) beats or equals (vb, ib)
+    const bool sw = key_beats(vb, ib, va, ia);
+    const float tv = sw ? vb : va;
+    const int ti = sw ? ib : ia;
+    vb = sw ? va : vb;
+    ib = sw ? ia : ib;
+    va = tv;
+    ia = ti;
+}
+
+__device__ void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
+    const int lane = threadIdx.x & 63;
+    float v0, v1, v2, v3;
+    int i0 = lane, i1 = lane + 64, i2 = lane + 128, i3 = lane + 192;
+    v0 = (i0 < E) ? l[i0] : -INFINITY;
+    v1 = (i1 < E) ? l[i1] : -INFINITY;
+    v2 = (i2 < E) ? l[i2] : -INFINITY;
+    v3 = (i3 < E) ? l[i3] : -INFINITY;
+    if (i0 >= E) i0 = 0x7FFFFFFF;
+    if (i1 >= E) i1 = 0x7FFFFFFF;
+    if (i2 >= E) i2 = 0x7FFFFFFF;
+    if (i3 >= E) i3 = 0x7FFFFFFF;
+    // sorting network for 4 keys
+    cswap(v0, i0, v1, i1);
+    cswap(v2, i2, v3, i3);
+    cswap(v0, i0, v2, i2);
+    cswap(v1, i1, v3, i3);
+    cswap(v1, i1, v2, i2);
+    float val[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s < K) {
+            const float m = wave_max_f32(v0);
+            const uint64_t hit = __ballot(v0 == m);
+            int gi;
+            if (__popcll(hit) == 1)  // usual case: one lane holds the maximum
+                gi = __builtin_amdgcn_readlane(i0, __ffsll((unsigned long long)hit) - 1);
+            else                     // equal logits: lowest expert index wins
+                gi = wave_min_i32(v0 == m ? i0 : 0x7FFFFFFF);
+            idx[s] = gi;
+            val[s] = m;
+            if (i0 == gi) {  // pop the head
+                v0 = v1; i0 = i1;
+                v1 = v2; i1 = i2;
+                v2 = v3; i2 = i3;
+                v3 = -INFINITY; i3 = 0x7FFFFFFF;
+            }
+        }
+    }
+    // softmax over the selected logits (val[0] is the largest)
+    float sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s < K) {
+            w[s] = __expf(val[s] - val[0]);
+            sum += w[s];
+        }
+    }
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+        if (s < K) w[s] *= inv;
+}
+
+// ---------------------------------------------------------------------------
 // router logits: one wave computes a TT-token x TE-expert tile
 // ---------------------------------------------------------------------------
 template <int TT, int TE>
@@ -68,73 +149,180 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
                 logits[(size_t)(t0 + t) * E + e0 + e] = acc[t][e];
 }
 
-hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
-                         hipStream_t st) {
-    if (T == 1) {
-        dim3 grid(1, (s.E + 3) / 4);
-        router_kernel<1, 1><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    } else if (T <= 16) {
-        dim3 grid(1, (s.E + 3) / 4);
-        router_kernel<16, 1><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    } else {
-        dim3 grid((T + 7) / 8, (s.E + 31) / 32);
-        router_kernel<8, 8><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+// ---------------------------------------------------------------------------
+// Small batches (T <= 16): router logits and the whole routing in one launch.
+//
+// Each wave computes one expert's logits for up to TT tokens, with every load
+// (MAXG 256-column groups of W and x) issued before the first FMA, in the same
+// summation order as router_kernel.  The block that finishes last (arrival
+// counter with device-scope release/acquire fences, reset by that block for
+// the next call) then does the routing with its 4 waves: top-k + softmax per
+// token, counts (LDS atomics: a count does not depend on order), a scan of
+// counts and of active flags (each lane of wave 0 owns 4 consecutive experts),
+// and a stable scatter where route r takes its rank among earlier routes of
+// the same expert.
+// ---------------------------------------------------------------------------
+// Needs blockDim.x >= E (one thread per expert).  Barriers order LDS only: the
+// global outputs are consumed by later kernels.
+__device__ void route_block(const float *__restrict__ logits, int T, int E, int K,
+                            int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+                            int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                            int32_t *__restrict__ active, int32_t *__restrict__ perm,
+                            int32_t *__restrict__ inv) {
+    __shared__ int s_idx[kDecodeMaxTokens * kMaxTopK];
+    __shared__ int s_wtot[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int R = T * K;
+    for (int t = wave; t < T; t += nw) {
+        int idx[kMaxTopK];
+        float w[kMaxTopK];
+        wave_topk(logits + (size_t)t * E, E, K, idx, w);
+        if (lane < K) {
+            int iv = idx[0];
+            float wv = w[0];
+#pragma unroll
+            for (int s = 1; s < kMaxTopK; ++s)
+                if (s < K && lane == s) { iv = idx[s]; wv = w[s]; }
+            idx_out[t * K + lane] = iv;
+            w_out[t * K + lane] = wv;
+            s_idx[t * K + lane] = iv;
+        }
     }
+    lds_barrier();
+    // expert e: its count and offset are direct counts over the <= 128 routes
+    const int e = tid;
+    int cnt = 0, below = 0;
+    if (e < E)
+        for (int r = 0; r < R; ++r) {
+            const int x = s_idx[r];
+            cnt += (x == e);
+            below += (x < e);
+        }
+    const bool act = e < E && cnt > 0;
+    const uint64_t mask = __ballot(act);
+    if (lane == 0) s_wtot[wave] = __popcll(mask);
+    // route r: its position is the number of routes ordered before it by
+    // (expert, route id) -- a stable grouping
+    for (int r = tid; r < R; r += blockDim.x) {
+        const int er = s_idx[r];
+        int pos = 0;
+        for (int r2 = 0; r2 < R; ++r2) {
+            const int x = s_idx[r2];
+            pos += (x < er) || (x == er && r2 < r);
+        }
+        perm[pos] = r;
+        inv[r] = pos;
+    }
+    lds_barrier();
+    if (e < E) {
+        counts[e] = cnt;
+        offsets[e] = below;
+        if (e == E - 1) offsets[E] = R;
+    }
+    int base = 0, tot = 0;
+    for (int q = 0; q < nw; ++q) {
+        base += (q < wave) ? s_wtot[q] : 0;
+        tot += s_wtot[q];
+    }
+    if (act) active[1 + base + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+    if (tid == 0) active[0] = tot;
+}
+
+template <int TT, int MAXG>
+__global__ __launch_bounds__(256) void router_route_small_kernel(
+    const uint16_t *__restrict__ x, const float *__restrict__ wr, int T, int H, int E, int K,
+    float *__restrict__ logits, uint32_t *__restrict__ arrivals, int32_t *__restrict__ idx_out,
+    float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int t0 = blockIdx.x * TT;
+    if (e < E) {
+        const int groups = H >> 8;
+        float4 wv[MAXG];
+        uint2 xb[TT][MAXG];
+#pragma unroll
+        for (int j = 0; j < MAXG; ++j)
+            if (j < groups)
+                wv[j] = *reinterpret_cast<const float4 *>(wr + (size_t)e * H + (j << 8) + (lane << 2));
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int j = 0; j < MAXG; ++j)
+                if (j < groups && t0 + t < T)
+                    xb[t][j] = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + t) * H + (j << 8) + (lane << 2));
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if (t0 + t >= T) break;
+            float a = 0.0f;
+#pragma unroll
+            for (int j = 0; j < MAXG; ++j) {
+                if (j < groups) {
+                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].x & 0xFFFFu), wv[j].x, a);
+                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].x >> 16), wv[j].y, a);
+                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].y & 0xFFFFu), wv[j].z, a);
+                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].y >> 16), wv[j].w, a);
+                }
+            }
+            a = wave_sum_xor(a, 1);
+            if (lane == 0) logits[(size_t)(t0 + t) * E + e] = a;
+        }
+    }
+    // last block to arrive does the routing
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = atomicAdd(arrivals, 1u);
+        s_last = (prev == gridDim.x * gridDim.y - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (threadIdx.x == 0) *arrivals = 0u;
+    route_block(logits, T, E, K, idx_out, w_out, counts, offsets, active, perm, inv);
+}
+
+template <int TT>
+static void router_route_launch(const Shape &s, dim3 grid, hipStream_t st, const uint16_t *x,
+                                const float *wr, int T, const Workspace &ws) {
+    const int g = s.H / 256;
+#define BQ_RR(G)                                                                               \
+    router_route_small_kernel<TT, G><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, s.K, ws.logits, \
+                                                           ws.arrivals, ws.idx, ws.w, ws.counts, \
+                                                           ws.offsets, ws.active, ws.perm, ws.inv)
+    if (g <= 1) BQ_RR(1);
+    else if (g <= 4) BQ_RR(4);
+    else if (g <= 16) BQ_RR(16);
+    else BQ_RR(32);
+#undef BQ_RR
+}
+
+__global__ void zero_u32_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_arrivals(const Workspace &ws, hipStream_t st) {
+    zero_u32_kernel<<<1, 64, 0, st>>>(ws.arrivals, 1);
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// top-k of one token by one wave
-// ---------------------------------------------------------------------------
-
-// (value, index) key: a beats b if its value is larger, or equal with a lower
-// index.  Comparing floats makes -0 and +0 equal, so they tie to the index.
-__device__ __forceinline__ bool key_beats(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
+                                     const Workspace &ws, hipStream_t st) {
+    if (T < 1 || T > kDecodeMaxTokens || s.H / 256 > 32) return hipErrorInvalidValue;
+    if (T == 1)
+        router_route_launch<1>(s, dim3(1, (s.E + 3) / 4), st, x, wr, T, ws);
+    else
+        router_route_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws);
+    return hipGetLastError();
 }
 
-// Selects the k best experts of `l` (E <= 256 logits) and their softmax
-// weights.  Every lane returns the same idx[]/val[]; lanes own experts
-// lane, lane+64, lane+128, lane+192.
-__device__ void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
-    const int lane = threadIdx.x & 63;
-    float v[4];
-    int id[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        id[q] = e;
-        v[q] = (e < E) ? l[e] : -INFINITY;
-    }
-    bool taken[4] = {false, false, false, false};
-    float val[kMaxTopK];
-    for (int s = 0; s < K; ++s) {
-        // best candidate of this lane
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (!taken[q] && id[q] < E && key_beats(v[q], id[q], bv, bi)) { bv = v[q]; bi = id[q]; }
-        // wave arg-best
-        for (int m = 1; m < 64; m <<= 1) {
-            const float ov = __shfl_xor(bv, m, 64);
-            const int oi = __shfl_xor(bi, m, 64);
-            if (key_beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (id[q] == bi) taken[q] = true;
-        idx[s] = bi;
-        val[s] = bv;
-    }
-    // softmax over the selected logits (val[0] is the largest)
-    float sum = 0.0f;
-    for (int s = 0; s < K; ++s) {
-        w[s] = __expf(val[s] - val[0]);
-        sum += w[s];
-    }
-    const float inv = 1.0f / sum;
-    for (int s = 0; s < K; ++s) w[s] *= inv;
+hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
+                         hipStream_t st) {
+    dim3 grid((T + 7) / 8, (s.E + 31) / 32);
+    router_kernel<8, 8><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    return hipGetLastError();
 }
 
 // one wave per token (prefill)
@@ -150,8 +338,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (lane < K) {
         int iv = idx[0];
         float wv = w[0];
-        for (int s = 1; s < K; ++s)
-            if (lane == s) { iv = idx[s]; wv = w[s]; }
+#pragma unroll
+        for (int s = 1; s < kMaxTopK; ++s)
+            if (s < K && lane == s) { iv = idx[s]; wv = w[s]; }
         idx_out[(size_t)t * K + lane] = iv;
         w_out[(size_t)t * K + lane] = wv;
     }
@@ -183,80 +372,6 @@ __device__ int block_exclusive_scan(int v, int *total, int *lds /* >= 16 ints */
     __syncthreads();
     *total = tot;
     return base + incl - v;
-}
-
-// ---------------------------------------------------------------------------
-// small batches (T <= 16): top-k, grouping and active-expert list in one block
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void route_small_kernel(const float *__restrict__ logits, int T,
-                                                           int E, int K, int32_t *__restrict__ idx_out,
-                                                           float *__restrict__ w_out,
-                                                           int32_t *__restrict__ counts,
-                                                           int32_t *__restrict__ offsets,
-                                                           int32_t *__restrict__ active,
-                                                           int32_t *__restrict__ perm,
-                                                           int32_t *__restrict__ inv,
-                                                           uint32_t *__restrict__ sync, int n_sync) {
-    __shared__ int s_idx[kDecodeMaxTokens * kMaxTopK];
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_off[kMaxExperts + 1];
-    __shared__ int s_scan[16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int R = T * K;
-
-    for (int i = tid; i < n_sync; i += blockDim.x) sync[i] = 0u;
-
-    if (wave < T) {
-        int idx[kMaxTopK];
-        float w[kMaxTopK];
-        wave_topk(logits + (size_t)wave * E, E, K, idx, w);
-        if (lane < K) {
-            int iv = idx[0];
-            float wv = w[0];
-            for (int s = 1; s < K; ++s)
-                if (lane == s) { iv = idx[s]; wv = w[s]; }
-            idx_out[wave * K + lane] = iv;
-            w_out[wave * K + lane] = wv;
-            s_idx[wave * K + lane] = iv;
-        }
-    }
-    __syncthreads();
-    // counts
-    int c = 0;
-    if (tid < E)
-        for (int r = 0; r < R; ++r) c += (s_idx[r] == tid);
-    int total;
-    const int off = block_exclusive_scan(tid < E ? c : 0, &total, s_scan);
-    if (tid < E) {
-        s_cnt[tid] = c;
-        s_off[tid] = off;
-        counts[tid] = c;
-        offsets[tid] = off;
-    }
-    if (tid == 0) offsets[E] = total;
-    // active experts, ascending
-    const int flag = (tid < E && c > 0) ? 1 : 0;
-    int n_active;
-    const int apos = block_exclusive_scan(flag, &n_active, s_scan);
-    if (flag) active[1 + apos] = tid;
-    if (tid == 0) active[0] = n_active;
-    __syncthreads();
-    // stable scatter: rank of route r among earlier routes of the same expert
-    if (tid < R) {
-        const int e = s_idx[tid];
-        int rank = 0;
-        for (int r = 0; r < tid; ++r) rank += (s_idx[r] == e);
-        const int p = s_off[e] + rank;
-        perm[p] = tid;
-        inv[tid] = p;
-    }
-}
-
-hipError_t launch_route_small(const Shape &s, int T, const Workspace &ws, hipStream_t st) {
-    route_small_kernel<<<1, 1024, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w, ws.counts,
-                                           ws.offsets, ws.active, ws.perm, ws.inv, ws.sync,
-                                           s.H / 16);
-    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -132,6 +132,31 @@ int moe_layer_routing(moe_layer *layer, int32_t *topk_idx, float *topk_w, int32_
  * MOE_EINVAL before the first forward. */
 int moe_layer_last_path(const moe_layer *layer);
 
+/* Kernel stages of a forward pass, in launch order. */
+enum {
+    MOE_STAGE_ROUTER = 0,  /* router logits (plus all of the routing for small batches) */
+    MOE_STAGE_SELECT = 1,  /* top-k + softmax (large batches) */
+    MOE_STAGE_PERMUTE = 2, /* counting sort of routes by expert (large batches) */
+    MOE_STAGE_GATEUP = 3,  /* gate/up projections + SwiGLU */
+    MOE_STAGE_DOWN = 4,    /* down projection (plus the combine for small batches) */
+    MOE_STAGE_COMBINE = 5, /* weighted combine (large batches) */
+    MOE_N_STAGES = 6
+};
+
+/* Measurement aid: per-stage kernel timing with HIP events.  slots > 0
+ * creates slots sets of event pairs; every later forward records, in the next
+ * slot (round robin), one event pair around each kernel it launches, on the
+ * forward's stream.  slots == 0 releases the events.  Creating events is a HIP
+ * runtime call, so this is not for use under stream capture.  Returns
+ * MOE_EINVAL for slots < 0 or > 65536, MOE_EHIP if event creation fails. */
+int moe_layer_set_profiling(moe_layer *layer, int32_t slots);
+
+/* Waits for the recorded events and writes elapsed milliseconds to the host
+ * array ms[slots][MOE_N_STAGES] (slot order = recording order modulo slots;
+ * -1 where a stage did not run).  slots must equal the value given to
+ * moe_layer_set_profiling. */
+int moe_layer_profile_read(moe_layer *layer, float *ms, int32_t slots);
+
 /* Release the handle (not the workspace).  NULL is a no-op. */
 void moe_layer_destroy(moe_layer *layer);
 
