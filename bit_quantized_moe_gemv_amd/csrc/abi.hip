@@ -1,9 +1,9 @@
-// abi.cpp -- the exported C entry points of libbqmoe.so: argument validation,
+// abi.hip -- the exported C entry points of libbqmoe.so: argument validation,
 // workspace carving and the launch sequence of one forward pass.
 #include <new>
 #include <vector>
 
-#include "../../include/bqmoe.h"
+#include "bqmoe.h"
 #include "moe_internal.h"
 
 using namespace bqmoe;
@@ -63,6 +63,12 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256(4);                       // arrivals
     b += align256(R * s.I * 4);             // h
     b += align256(R * s.H * 4);             // y
+    if (s.fmt == MOE_FMT_VQ13R8) {
+        b += align256((size_t)tmax * s.H * 2);  // x16
+        b += align256((size_t)tmax * 4);        // xexp
+        b += align256(R * s.I * 2);             // h16
+        b += align256(R * 4);                   // hexp
+    }
     return b;
 }
 
@@ -85,6 +91,16 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->arrivals = reinterpret_cast<uint32_t *>(take(4));
     ws->h = take(R * s.I * 4);
     ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
+    ws->x16 = nullptr;
+    ws->xexp = nullptr;
+    ws->h16 = nullptr;
+    ws->hexp = nullptr;
+    if (s.fmt == MOE_FMT_VQ13R8) {
+        ws->x16 = reinterpret_cast<uint16_t *>(take((size_t)tmax * s.H * 2));
+        ws->xexp = reinterpret_cast<int32_t *>(take((size_t)tmax * 4));
+        ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
+        ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));
+    }
 }
 
 }  // namespace bqmoe
@@ -101,7 +117,6 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
         if (d->inter % 128) return MOE_EINVAL;
     } else if (d->format == MOE_FMT_VQ13R8) {
         if (d->inter % 256) return MOE_EINVAL;
-        return MOE_EUNSUPPORTED;  // VQ kernels not built yet
     } else {
         return MOE_EINVAL;
     }
@@ -219,12 +234,17 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
             err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_PERMUTE, st, [&] { return launch_permute(s, T, ws, st); });
+        const bool vq = s.fmt == MOE_FMT_VQ13R8;
         if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_GATEUP, st,
-                         [&] { return launch_prefill_gateup(s, T, x, packed, ws, st); });
+            err = staged(L, slot, MOE_STAGE_GATEUP, st, [&] {
+                return vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
+                          : launch_prefill_gateup(s, T, x, packed, ws, st);
+            });
         if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_DOWN, st,
-                         [&] { return launch_prefill_down(s, T, packed, ws, st); });
+            err = staged(L, slot, MOE_STAGE_DOWN, st, [&] {
+                return vq ? launch_vq_prefill_down(s, T, packed, ws, st)
+                          : launch_prefill_down(s, T, packed, ws, st);
+            });
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_COMBINE, st,
                          [&] { return launch_combine(s, T, ws, out, st); });

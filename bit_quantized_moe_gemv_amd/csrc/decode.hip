@@ -330,7 +330,7 @@ bool decode_supported(const Shape &s) {
     const int nj = s.H / 256;
     const bool h_ok = nj == 1 || nj == 2 || nj == 4 || nj == 8 || nj == 16 || nj == 32;
     const bool i_ok = s.I == 128 || s.I == 256 || s.I == 512 || s.I == 1024 || s.I == 2048;
-    return h_ok && i_ok;
+    return s.fmt == MOE_FMT_MXFP4 && h_ok && i_ok;
 }
 
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "bqmoe.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -40,8 +42,13 @@ struct Workspace {
     int32_t *perm;     // [Rmax]
     int32_t *inv;      // [Rmax]
     uint32_t *arrivals;  // [1] block arrival counter of the small-batch router
-    void *h;           // [Rmax][I] fp32 (decode) or two [Rmax][I] bf16 arrays (prefill)
+    void *h;           // [Rmax][I]: fp32 (decode, VQ prefill) or two bf16 arrays (MXFP4 prefill)
     float *y;          // [Rmax][H] fp32 per-route expert outputs
+    // VQ prefill only (null otherwise): fp16 rows with a power-of-two exponent each
+    uint16_t *x16;     // [Tmax][H]
+    int32_t *xexp;     // [Tmax]
+    uint16_t *h16;     // [Rmax][I]
+    int32_t *hexp;     // [Rmax]
 };
 
 size_t workspace_bytes(const Shape &s, int tmax);
@@ -64,6 +71,10 @@ hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const
                                  const Workspace &ws, hipStream_t st);
 hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                                hipStream_t st);
+hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
+                                    const uint8_t *packed, const Workspace &ws, hipStream_t st);
+hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
+                                  const Workspace &ws, hipStream_t st);
 hipError_t launch_combine(const Shape &s, int T, const Workspace &ws, float *out, hipStream_t st);
 
 // ---- device helpers ----

@@ -113,3 +113,25 @@ def test_forced_decode_rejects_large_batches(lib):
         assert lib.moe_layer_forward(h, fake, 17, fake, fake, fake, None) == bq.MOE_EINVAL
     finally:
         lib.moe_layer_destroy(h)
+
+
+def test_vq_descriptor_sizes_and_paths(lib):
+    """VQ13R8 layers: packed size = books + experts; intermediate widths must be
+    multiples of 256; the batch-1 decode kernels are MXFP4-only, so forcing
+    the decode path on a VQ layer is reported as unsupported."""
+    import workloads as W
+    for h, i, e in ((256, 256, 8), (4096, 2048, 256)):
+        assert bq.packed_size(h, i, e, 2, fmt=bq.MOE_FMT_VQ13R8) == \
+            W.packed_bytes(W.FMT_VQ13R8, h, i, e)
+    with pytest.raises(bq.MoeError) as ei:
+        bq.packed_size(256, 128, 8, 2, fmt=bq.MOE_FMT_VQ13R8)
+    assert ei.value.status == bq.MOE_EINVAL
+    with pytest.raises(bq.MoeError) as ei:
+        bq.workspace_size(256, 256, 8, 2, 16, bq.MOE_FMT_VQ13R8, bq.MOE_PATH_DECODE)
+    assert ei.value.status == bq.MOE_EUNSUPPORTED
+    # the VQ workspace adds the fp16 copies of x and h and their row exponents
+    mx = bq.workspace_size(4096, 2048, 256, 8, 2048, bq.MOE_FMT_MXFP4)
+    vq = bq.workspace_size(4096, 2048, 256, 8, 2048, bq.MOE_FMT_VQ13R8)
+    r = 2048 * 8
+    assert vq - mx >= 2048 * 4096 * 2 + r * 2048 * 2 + (2048 + r) * 4
+    assert vq - mx < 2048 * 4096 * 2 + r * 2048 * 2 + (2048 + r) * 4 + 4 * 256
