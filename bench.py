@@ -11,9 +11,12 @@ Cache protocol: the 256 MB last-level cache could hold a decode step's
 and every step takes a fresh token; a reused expert is then never still cached.
 
 Prints ONE JSON line (rank 0): metric/value (tokens/s), roofline of the
-dominant kernel (HIP events around each of its launches on its own stream),
-the CPU oracle timed on a bounded sample, and extra workloads (16-token
-verify with skewed routing, 2048-token prefill) with their own rooflines.
+dominant kernel, the CPU oracle timed on a bounded sample, and extra workloads
+(16-token verify with skewed routing, 2048-token MXFP4 and VQ13R8 prefill)
+with their own rooflines.  A kernel's launch duration is measured with two HIP
+events on the stream it runs on around `steps` back-to-back launches of it
+(moe_layer_replay_stage over the last step's routing, cycling the layer
+copies), so it compares directly with a rocprofv3 kernel trace.
 """
 
 from __future__ import annotations
@@ -100,12 +103,35 @@ class Bench:
         t0 = time.perf_counter()
         self.host_layer = W.make_experts(base)
         log(f"  {time.perf_counter() - t0:.1f}s; copying {args.layers} device copies")
-        src = torch.from_numpy(self.host_layer)
-        self.layers = [src.to("cuda") for _ in range(args.layers)]
+        self.layers = self._copies(self.host_layer, args.layers)
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
 
-    def run(self, wl, steps, warmup, tokens_per_step, profile=True):
+    def _copies(self, host, n):
+        """n device copies of a packed layer, back to back in one allocation:
+        (tensor, base pointer, stride in bytes, n)."""
+        torch = self.torch
+        nb = host.nbytes
+        stride = (nb + 255) // 256 * 256
+        big = torch.empty(stride * n, dtype=torch.uint8, device="cuda")
+        src = torch.from_numpy(host).to("cuda")
+        for i in range(n):
+            big[i * stride:i * stride + nb].copy_(src)
+        del src
+        return big, int(big.data_ptr()), stride, n
+
+    def vq_layers(self):
+        """One device copy of the VQ13R8 layer (2.1 GB: larger than every cache)."""
+        if not hasattr(self, "_vq"):
+            W, torch = self.W, self.torch
+            log(f"generating the MiMo-shaped VQ13R8 layer ({W.VQ_PREFILL.packed_bytes} B)")
+            host = W.make_experts(W.VQ_PREFILL)
+            self._vq = self._copies(host, 1)
+            del host
+            torch.cuda.synchronize()
+        return self._vq
+
+    def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0):
         torch, bq, W = self.torch, self.bq, self.W
         T = tokens_per_step
         n_batches = steps + warmup
@@ -121,9 +147,9 @@ class Bench:
         layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt)
         out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
         st = self.stream.cuda_stream
-        L = len(self.layers)
+        _, base, stride, L = self.layers if layers is None else layers
         xp = [int(xall[i].data_ptr()) for i in range(n_batches)]
-        lp = [int(t.data_ptr()) for t in self.layers]
+        lp = [base + i * stride for i in range(L)]
         wp, op = int(wr.data_ptr()), int(out.data_ptr())
 
         def loop(i0, n):
@@ -144,6 +170,22 @@ class Bench:
         r = layer.routing()
         counts = r.counts.cpu()
         res["distinct_experts_last_step"] = int((counts > 0).sum())
+        if replay:
+            # each expert kernel alone: `replay` back-to-back launches of one
+            # stage of the last step (cycling the layer copies) between two
+            # events on the stream the kernels run on
+            res["replay_us"] = {}
+            for stage in ("gateup", "down"):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                rc = layer.replay_stage_raw(stage, replay, xp[warmup + steps - 1], base, stride,
+                                            L, op, st)
+                e1.record(self.stream)
+                if rc != 0:
+                    raise bq.MoeError(rc, "moe_layer_replay_stage")
+                e1.synchronize()
+                res["replay_us"][stage] = round(e0.elapsed_time(e1) * 1e3 / replay, 3)
         if profile:
             # second pass over the same steps with event pairs around each kernel
             layer.set_profiling(steps)
@@ -164,11 +206,16 @@ class Bench:
 
 def algorithmic(wl, distinct, T):
     """Algorithmic bytes / flops of the gate/up and down kernels and the whole
-    step.  Per expert: gate/up 2*I*H*17/32 bytes, down H*I*17/32 bytes."""
+    step.  Per expert: MXFP4 gate/up 2*I*H*17/32 bytes and down H*I*17/32
+    bytes; VQ13R8 21/64 byte per weight plus an fp16 gain per row."""
     H, I, k = wl.hidden, wl.inter, wl.top_k
     R = T * k
-    gu_e = 2 * I * H * 17 // 32
-    dn_e = H * I * 17 // 32
+    if wl.fmt == W_FMT_VQ:
+        gu_e = 2 * I * H * 21 // 64 + 2 * (2 * I)
+        dn_e = H * I * 21 // 64 + 2 * H
+    else:
+        gu_e = 2 * I * H * 17 // 32
+        dn_e = H * I * 17 // 32
     gateup_bytes = distinct * gu_e + T * H * 2 + R * I * 4
     down_bytes = distinct * dn_e + R * I * 4 + T * H * 4
     step_bytes = distinct * (gu_e + dn_e) + wl.experts * H * 4 + T * H * 2 + T * H * 4
@@ -176,6 +223,23 @@ def algorithmic(wl, distinct, T):
     flops_dn = 2 * R * H * I
     return dict(gateup_bytes=gateup_bytes, down_bytes=down_bytes, step_bytes=step_bytes,
                 gateup_flops=flops_gu, down_flops=flops_dn, step_flops=flops_gu + flops_dn)
+
+
+W_FMT_VQ = 2
+
+
+def prefill_report(pre, a):
+    pf = a["step_flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
+    gu_t = a["gateup_flops"] / (pre["replay_us"]["gateup"] * 1e-6) / 1e12
+    dn_t = a["down_flops"] / (pre["replay_us"]["down"] * 1e-6) / 1e12
+    return {
+        **pre, "step_algorithmic_flops": a["step_flops"],
+        "step_algorithmic_bytes": a["step_bytes"],
+        "step_mfma_tflops": round(pf, 1), "step_mfma_frac": round(pf / BF16_PEAK_TFLOPS, 4),
+        "step_hbm_frac": round(a["step_bytes"] / (pre["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "gateup_mfma_frac": round(gu_t / BF16_PEAK_TFLOPS, 4),
+        "down_mfma_frac": round(dn_t / BF16_PEAK_TFLOPS, 4),
+    }
 
 
 def cpu_baseline(host_layer, W, n_tokens):
@@ -198,11 +262,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--layers", type=int, default=4, help="device copies of the layer cycled")
+    ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode only")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "copy"],
+                    default=None,
                     help="run one workload without the report (for profilers)")
     ap.add_argument("--no-peaks", action="store_true")
     args = ap.parse_args()
@@ -221,19 +286,32 @@ def main():
     bq.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        # a plain device copy of known size (1 GiB read + 1 GiB written per
+        # launch): the reference that scales HBM byte counters
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device="cuda")
+        c = torch.empty_like(a)
+        for _ in range(args.steps):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        log(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
     b = Bench(args, torch, bq, W)
 
     if args.only:
-        wl = {"decode": W.DECODE, "verify": W.VERIFY, "prefill": W.PREFILL}[args.only]
-        res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False)
+        wl = {"decode": W.DECODE, "verify": W.VERIFY, "prefill": W.PREFILL,
+              "vq_prefill": W.VQ_PREFILL}[args.only]
+        res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False,
+                    layers=b.vq_layers() if wl.fmt == W_FMT_VQ else None)
         log(json.dumps(res))
         return
 
     log("decode T=1")
-    dec = b.run(W.DECODE, args.steps, args.warmup, 1)
+    dec = b.run(W.DECODE, args.steps, args.warmup, 1, replay=args.steps)
     wl = W.DECODE
     alg = algorithmic(wl, dec["distinct_experts_last_step"], 1)
-    gu_us = dec["stage_us"]["gateup"]
+    gu_us = dec["replay_us"]["gateup"]
     achieved = alg["gateup_bytes"] / (gu_us * 1e-6) / 1e9
     roof = {"kernel": "decode_gateup_mxfp4", "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -243,7 +321,7 @@ def main():
     extra = {"decode_t1": {**dec, "step_algorithmic_bytes": alg["step_bytes"],
                            "step_hbm_gbs": round(step_gbs, 1),
                            "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                           "down_hbm_gbs": round(alg["down_bytes"] / (dec["stage_us"]["down"] * 1e-6) / 1e9, 1)}}
+                           "down_hbm_gbs": round(alg["down_bytes"] / (dec["replay_us"]["down"] * 1e-6) / 1e9, 1)}}
 
     if not args.no_extra:
         log("verify T=16 (skewed routing)")
@@ -252,18 +330,12 @@ def main():
         extra["verify_t16"] = {**ver, "step_algorithmic_bytes": a["step_bytes"],
                                "step_hbm_gbs": round(a["step_bytes"] / (ver["ms_per_step"] * 1e-3) / 1e9, 1)}
         log("prefill T=2048")
-        pre = b.run(W.PREFILL, 30, 5, 2048)
-        a = algorithmic(W.PREFILL, W.PREFILL.experts, 2048)
-        pf = a["step_flops"] / (pre["ms_per_step"] * 1e-3) / 1e12
-        gu_t = a["gateup_flops"] / (pre["stage_us"]["gateup"] * 1e-6) / 1e12
-        dn_t = a["down_flops"] / (pre["stage_us"]["down"] * 1e-6) / 1e12
-        extra["prefill_t2048"] = {
-            **pre, "step_algorithmic_flops": a["step_flops"],
-            "step_mfma_tflops": round(pf, 1), "step_mfma_frac": round(pf / BF16_PEAK_TFLOPS, 4),
-            "step_hbm_frac": round(a["step_bytes"] / (pre["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "gateup_mfma_frac": round(gu_t / BF16_PEAK_TFLOPS, 4),
-            "down_mfma_frac": round(dn_t / BF16_PEAK_TFLOPS, 4),
-        }
+        pre = b.run(W.PREFILL, 30, 5, 2048, replay=10)
+        extra["prefill_t2048"] = prefill_report(pre, algorithmic(W.PREFILL, W.PREFILL.experts, 2048))
+        log("VQ13R8 prefill T=2048")
+        vq = b.run(W.VQ_PREFILL, 30, 5, 2048, layers=b.vq_layers(), replay=10)
+        extra["vq_prefill_t2048"] = prefill_report(
+            vq, algorithmic(W.VQ_PREFILL, W.VQ_PREFILL.experts, 2048))
     if not args.no_peaks:
         extra["measured_peaks"] = measured_peaks(torch)
 

@@ -274,6 +274,37 @@ int moe_layer_routing(moe_layer *L, int32_t *topk_idx, float *topk_w, int32_t *c
     return MOE_OK;
 }
 
+int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void *x_bf16,
+                           const void *packed_experts, size_t copy_stride, int32_t n_copies,
+                           float *out, void *hip_stream) {
+    if (!L || L->last_T < 1) return MOE_EINVAL;
+    if (stage != MOE_STAGE_GATEUP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
+    if (reps < 1 || n_copies < 1 || (copy_stride & 15u)) return MOE_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(packed_experts) || !aligned16(out)) return MOE_EINVAL;
+    const Shape &s = L->shape;
+    const Workspace &ws = L->ws;
+    const int T = L->last_T;
+    const bool vq = s.fmt == MOE_FMT_VQ13R8;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    for (int i = 0; i < reps; ++i) {
+        const uint8_t *packed =
+            static_cast<const uint8_t *>(packed_experts) + (size_t)(i % n_copies) * copy_stride;
+        hipError_t e;
+        if (L->last_path == MOE_PATH_DECODE)
+            e = stage == MOE_STAGE_GATEUP ? launch_decode_gateup(s, T, x, packed, ws, st)
+                                          : launch_decode_down(s, T, packed, ws, out, st);
+        else if (stage == MOE_STAGE_GATEUP)
+            e = vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
+                   : launch_prefill_gateup(s, T, x, packed, ws, st);
+        else
+            e = vq ? launch_vq_prefill_down(s, T, packed, ws, st)
+                   : launch_prefill_down(s, T, packed, ws, st);
+        if (e != hipSuccess) return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
 int moe_layer_last_path(const moe_layer *L) { return L && L->last_T > 0 ? L->last_path : MOE_EINVAL; }
 
 int moe_layer_set_profiling(moe_layer *L, int32_t slots) {

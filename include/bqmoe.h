@@ -65,14 +65,25 @@ enum {
  *   column j) is at stream position ((j/8)*16 + r)*8 + j%8 of its tile; code12
  *   is a little-endian 12-bit stream, plane a little-endian bit stream (bit 12
  *   of the index), res one byte per vector; gains are one fp16 per row.
- *   Weight w[n][8v+d] = gain[n] * (Cb[i13][d] + Rb[i8][d]).
+ *   Weight w[n][8v+d] = gain[n] * (Cb[i13][d] + Rb[i8][d]); every sum
+ *   Cb[i][d] + Rb[j][d] must be finite in fp16 (|sum| <= 65504).
  */
 enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2 };
 
 /* Path selection: AUTO uses the weight-streaming decode kernels for batches of
  * at most MOE_DECODE_MAX_TOKENS tokens and the grouped-GEMM prefill kernels
  * above that; DECODE and PREFILL force one of them (DECODE requires
- * T <= MOE_DECODE_MAX_TOKENS). */
+ * T <= MOE_DECODE_MAX_TOKENS).  The decode kernels exist for MXFP4 layers
+ * with hidden/256 and inter powers of two (inter <= 2048): other layers,
+ * VQ13R8 ones included, run the grouped-GEMM kernels at every batch size, and
+ * forcing DECODE on them returns MOE_EUNSUPPORTED.
+ *
+ * Numerics of the grouped-GEMM kernels: MXFP4 weights are exact in bf16 and
+ * the intermediate h enters the down projection as an exact bf16 pair
+ * (hi + lo); VQ13R8 weights enter as fp16(Cb + Rb) (one rounding, relative
+ * error <= 2^-11) with the row gain applied in fp32, and x and h as fp16 rows
+ * scaled by an exact power of two per row (relative error <= 2^-11 for h).
+ * All products accumulate in fp32. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 #define MOE_DECODE_MAX_TOKENS 16
 
@@ -94,7 +105,9 @@ int moe_workspace_size(const moe_layer_desc *desc, size_t *bytes);
 
 /* Validate desc and bind a caller-owned device workspace (256-byte aligned,
  * at least moe_workspace_size bytes, kept alive until moe_layer_destroy).
- * Writes a new handle to *out.  Makes no device call. */
+ * Writes a new handle to *out.  Makes no device call (the first decode-path
+ * forward on a handle enqueues one small kernel that zeroes a counter in the
+ * workspace). */
 int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
                      moe_layer **out);
 
@@ -156,6 +169,22 @@ int moe_layer_set_profiling(moe_layer *layer, int32_t slots);
  * -1 where a stage did not run).  slots must equal the value given to
  * moe_layer_set_profiling. */
 int moe_layer_profile_read(moe_layer *layer, float *ms, int32_t slots);
+
+/* Measurement aid: enqueue the kernels of one stage of the last forward
+ * (MOE_STAGE_GATEUP or MOE_STAGE_DOWN) `reps` times back to back on
+ * hip_stream, reusing that forward's routing, so that events around the call
+ * time the stage's kernels alone.  Repetition i reads the layer at
+ * packed_experts + (i % n_copies) * copy_stride (cycling through copies keeps
+ * the weights from being served by the last-level cache); x_bf16 and out are
+ * the last forward's token rows and output ([T][hidden], same alignment rules
+ * as moe_layer_forward; out is only written by the decode down stage).  The
+ * stage's results are those of the last forward again.  Returns MOE_EINVAL
+ * before the first forward, for another stage, reps < 1, n_copies < 1,
+ * a copy_stride not a multiple of 16, or a bad pointer; MOE_EHIP if a launch
+ * fails. */
+int moe_layer_replay_stage(moe_layer *layer, int32_t stage, int32_t reps, const void *x_bf16,
+                           const void *packed_experts, size_t copy_stride, int32_t n_copies,
+                           float *out, void *hip_stream);
 
 /* Release the handle (not the workspace).  NULL is a no-op. */
 void moe_layer_destroy(moe_layer *layer);

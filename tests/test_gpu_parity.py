@@ -160,3 +160,31 @@ def test_mimo_prefill_2048(torch_dev):
     sample = sorted(set(scaled[:3].tolist()) | {0, 1000, 2047})
     got = _sampled_check(torch_dev, wl, PRE, sample)
     assert got["counts"].sum() == wl.tokens * wl.top_k
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+def test_replay_stage_reproduces_forward(torch_dev, path):
+    """moe_layer_replay_stage re-runs a stage of the last forward: replaying
+    gate/up and down (and, for large batches, re-running the combine through a
+    second forward) leaves the output bit-identical."""
+    from gpu_harness import Runner
+    import bit_quantized_moe_gemv_amd as bq
+    torch = torch_dev
+    wl = W.TINY.replace(tokens=5 if path == DEC else 90, seed=31)
+    x, wr = W.make_x(wl), W.make_router(wl)
+    run = Runner(wl, path)
+    ref = run.run(x, wr)["out"]
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.from_numpy(ref.astype(np.float32)).cuda()
+    st = torch.cuda.current_stream().cuda_stream
+    layer = run.layer
+    run.layer.forward(xd, torch.from_numpy(wr).cuda(), run.packed, out=out)
+    for stage in ("gateup", "down"):
+        rc = layer.replay_stage_raw(stage, 3, int(xd.data_ptr()), int(run.packed.data_ptr()),
+                                    0, 1, int(out.data_ptr()), st)
+        assert rc == bq.MOE_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+    bad = layer.replay_stage_raw("router", 1, int(xd.data_ptr()), int(run.packed.data_ptr()),
+                                 0, 1, int(out.data_ptr()), st)
+    assert bad == bq.MOE_EINVAL
