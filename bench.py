@@ -175,12 +175,14 @@ class Bench:
             # stage of the last step (cycling the layer copies) between two
             # events on the stream the kernels run on
             res["replay_us"] = {}
-            for stage in ("gateup", "down"):
+            stages = (("router", "gateup", "down") if layer.last_path() == bq.MOE_PATH_DECODE
+                      else bq.STAGES)
+            for stage in stages:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(self.stream)
-                rc = layer.replay_stage_raw(stage, replay, xp[warmup + steps - 1], base, stride,
-                                            L, op, st)
+                rc = layer.replay_stage_raw(stage, replay, xp[warmup + steps - 1], wp, base,
+                                            stride, L, op, st)
                 e1.record(self.stream)
                 if rc != 0:
                     raise bq.MoeError(rc, "moe_layer_replay_stage")

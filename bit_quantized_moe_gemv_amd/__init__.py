@@ -98,7 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_layer_set_profiling.restype = ctypes.c_int
     lib.moe_layer_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]
     lib.moe_layer_profile_read.restype = ctypes.c_int
-    lib.moe_layer_replay_stage.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P,
+    lib.moe_layer_replay_stage.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P,
                                            ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.moe_layer_replay_stage.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -205,13 +205,14 @@ class MoeLayer:
         return self._lib.moe_layer_forward(self._handle, x_ptr, T, router_ptr, packed_ptr,
                                            out_ptr, ctypes.c_void_p(stream_ptr))
 
-    def replay_stage_raw(self, stage: str, reps: int, x_ptr: int, packed_ptr: int,
-                         copy_stride: int, n_copies: int, out_ptr: int, stream_ptr: int) -> int:
-        """Re-run one stage ("gateup" or "down") of the last forward reps times
+    def replay_stage_raw(self, stage: str, reps: int, x_ptr: int, router_ptr: int,
+                         packed_ptr: int, copy_stride: int, n_copies: int, out_ptr: int,
+                         stream_ptr: int) -> int:
+        """Re-run one stage (a name in STAGES) of the last forward reps times
         (moe_layer_replay_stage); returns the status code."""
         return self._lib.moe_layer_replay_stage(
-            self._handle, STAGES.index(stage), reps, x_ptr, packed_ptr, copy_stride, n_copies,
-            out_ptr, ctypes.c_void_p(stream_ptr))
+            self._handle, STAGES.index(stage), reps, x_ptr, router_ptr, packed_ptr, copy_stride,
+            n_copies, out_ptr, ctypes.c_void_p(stream_ptr))
 
     def routing(self, stream=None) -> Routing:
         import torch

@@ -16,7 +16,6 @@ struct moe_layer {
     Workspace ws;
     int last_T;
     int last_path;
-    bool arrivals_ready;  // the router's arrival counter has been zeroed on the device
     // per-stage timing (moe_layer_set_profiling)
     int prof_slots;
     int prof_next;
@@ -60,7 +59,6 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256((size_t)(s.E + 1) * 4);   // active
     b += align256(R * 4);                   // perm
     b += align256(R * 4);                   // inv
-    b += align256(4);                       // arrivals
     b += align256(R * s.I * 4);             // h
     b += align256(R * s.H * 4);             // y
     if (s.fmt == MOE_FMT_VQ13R8) {
@@ -88,7 +86,6 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->active = reinterpret_cast<int32_t *>(take((size_t)(s.E + 1) * 4));
     ws->perm = reinterpret_cast<int32_t *>(take(R * 4));
     ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
-    ws->arrivals = reinterpret_cast<uint32_t *>(take(4));
     ws->h = take(R * s.I * 4);
     ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
     ws->x16 = nullptr;
@@ -180,7 +177,6 @@ int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_byte
     carve_workspace(s, desc->max_tokens, workspace, &L->ws);
     L->last_T = 0;
     L->last_path = MOE_EINVAL;
-    L->arrivals_ready = false;
     L->prof_slots = 0;
     L->prof_next = 0;
     *out = L;
@@ -213,13 +209,7 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
     }
     hipError_t err = hipSuccess;
     if (path == MOE_PATH_DECODE) {
-        if (!L->arrivals_ready) {
-            // once per handle: the counter then resets itself at the end of every call
-            err = launch_zero_arrivals(ws, st);
-            if (err == hipSuccess) L->arrivals_ready = true;
-        }
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_ROUTER, st,
+        err = staged(L, slot, MOE_STAGE_ROUTER, st,
                          [&] { return launch_router_route_small(s, x, router_w, T, ws, st); });
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_GATEUP, st,
@@ -275,12 +265,18 @@ int moe_layer_routing(moe_layer *L, int32_t *topk_idx, float *topk_w, int32_t *c
 }
 
 int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void *x_bf16,
-                           const void *packed_experts, size_t copy_stride, int32_t n_copies,
-                           float *out, void *hip_stream) {
+                           const float *router_w, const void *packed_experts, size_t copy_stride,
+                           int32_t n_copies, float *out, void *hip_stream) {
     if (!L || L->last_T < 1) return MOE_EINVAL;
-    if (stage != MOE_STAGE_GATEUP && stage != MOE_STAGE_DOWN) return MOE_EINVAL;
+    if (stage < 0 || stage >= MOE_N_STAGES) return MOE_EINVAL;
+    const bool decode = L->last_path == MOE_PATH_DECODE;
+    if (decode && (stage == MOE_STAGE_SELECT || stage == MOE_STAGE_PERMUTE ||
+                   stage == MOE_STAGE_COMBINE))
+        return MOE_EINVAL;
     if (reps < 1 || n_copies < 1 || (copy_stride & 15u)) return MOE_EINVAL;
-    if (!aligned16(x_bf16) || !aligned16(packed_experts) || !aligned16(out)) return MOE_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(router_w) || !aligned16(packed_experts) ||
+        !aligned16(out))
+        return MOE_EINVAL;
     const Shape &s = L->shape;
     const Workspace &ws = L->ws;
     const int T = L->last_T;
@@ -290,16 +286,26 @@ int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void
     for (int i = 0; i < reps; ++i) {
         const uint8_t *packed =
             static_cast<const uint8_t *>(packed_experts) + (size_t)(i % n_copies) * copy_stride;
-        hipError_t e;
-        if (L->last_path == MOE_PATH_DECODE)
-            e = stage == MOE_STAGE_GATEUP ? launch_decode_gateup(s, T, x, packed, ws, st)
-                                          : launch_decode_down(s, T, packed, ws, out, st);
-        else if (stage == MOE_STAGE_GATEUP)
-            e = vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
-                   : launch_prefill_gateup(s, T, x, packed, ws, st);
-        else
-            e = vq ? launch_vq_prefill_down(s, T, packed, ws, st)
-                   : launch_prefill_down(s, T, packed, ws, st);
+        hipError_t e = hipSuccess;
+        switch (stage) {
+            case MOE_STAGE_ROUTER:
+                e = decode ? launch_router_route_small(s, x, router_w, T, ws, st)
+                           : launch_router(s, x, router_w, T, ws.logits, st);
+                break;
+            case MOE_STAGE_SELECT: e = launch_topk(s, T, ws, st); break;
+            case MOE_STAGE_PERMUTE: e = launch_permute(s, T, ws, st); break;
+            case MOE_STAGE_GATEUP:
+                e = decode ? launch_decode_gateup(s, T, x, packed, ws, st)
+                    : vq   ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
+                           : launch_prefill_gateup(s, T, x, packed, ws, st);
+                break;
+            case MOE_STAGE_DOWN:
+                e = decode ? launch_decode_down(s, T, packed, ws, out, st)
+                    : vq   ? launch_vq_prefill_down(s, T, packed, ws, st)
+                           : launch_prefill_down(s, T, packed, ws, st);
+                break;
+            default: e = launch_combine(s, T, ws, out, st); break;
+        }
         if (e != hipSuccess) return MOE_EHIP;
     }
     return MOE_OK;

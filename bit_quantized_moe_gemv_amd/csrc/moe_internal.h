@@ -41,7 +41,6 @@ struct Workspace {
     int32_t *active;   // [1 + E]: n_active, then active experts ascending
     int32_t *perm;     // [Rmax]
     int32_t *inv;      // [Rmax]
-    uint32_t *arrivals;  // [1] block arrival counter of the small-batch router
     void *h;           // [Rmax][I]: fp32 (decode, VQ prefill) or two bf16 arrays (MXFP4 prefill)
     float *y;          // [Rmax][H] fp32 per-route expert outputs
     // VQ prefill only (null otherwise): fp16 rows with a power-of-two exponent each
@@ -59,7 +58,6 @@ hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int
                          hipStream_t st);
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
                                      const Workspace &ws, hipStream_t st);
-hipError_t launch_zero_arrivals(const Workspace &ws, hipStream_t st);
 hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 bool decode_supported(const Shape &s);

@@ -150,27 +150,27 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Small batches (T <= 16): router logits and the whole routing in one launch.
+// Small batches (T <= 16): router logits, then the whole routing in one block.
 //
-// Each wave computes one expert's logits for up to TT tokens, with every load
-// (MAXG 256-column groups of W and x) issued before the first FMA, in the same
-// summation order as router_kernel.  The block that finishes last (arrival
-// counter with device-scope release/acquire fences, reset by that block for
-// the next call) then does the routing with its 4 waves: top-k + softmax per
-// token, counts (LDS atomics: a count does not depend on order), a scan of
-// counts and of active flags (each lane of wave 0 owns 4 consecutive experts),
-// and a stable scatter where route r takes its rank among earlier routes of
-// the same expert.
+// router_small_kernel: each wave computes one expert's logits for up to TT
+// tokens, with every load (MAXG 256-column groups of W and x) issued before the
+// first FMA, in the same summation order as router_kernel.
+//
+// route_small_kernel (one block of 16 waves): top-k + softmax, one wave per
+// token; counts (a count does not depend on order); the active list (ballot
+// prefix over experts); and a stable grouping in which route r takes its rank
+// among earlier routes of the same expert.  A separate launch costs less than
+// publishing the logits across the XCDs from inside the router kernel (a
+// device-scope release per block plus an arrival counter).
 // ---------------------------------------------------------------------------
-// Needs blockDim.x >= E (one thread per expert).  Barriers order LDS only: the
-// global outputs are consumed by later kernels.
-__device__ void route_block(const float *__restrict__ logits, int T, int E, int K,
-                            int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-                            int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                            int32_t *__restrict__ active, int32_t *__restrict__ perm,
-                            int32_t *__restrict__ inv) {
+constexpr int kRouteThreads = 1024;
+
+__global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
+    const float *__restrict__ logits, int T, int E, int K, int32_t *__restrict__ idx_out,
+    float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
     __shared__ int s_idx[kDecodeMaxTokens * kMaxTopK];
-    __shared__ int s_wtot[16];
+    __shared__ int s_wtot[kRouteThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = T * K;
     for (int t = wave; t < T; t += nw) {
@@ -229,92 +229,67 @@ __device__ void route_block(const float *__restrict__ logits, int T, int E, int 
 }
 
 template <int TT, int MAXG>
-__global__ __launch_bounds__(256) void router_route_small_kernel(
-    const uint16_t *__restrict__ x, const float *__restrict__ wr, int T, int H, int E, int K,
-    float *__restrict__ logits, uint32_t *__restrict__ arrivals, int32_t *__restrict__ idx_out,
-    float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
-    __shared__ int s_last;
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ wr, int T,
+                                                           int H, int E,
+                                                           float *__restrict__ logits) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int t0 = blockIdx.x * TT;
-    if (e < E) {
-        const int groups = H >> 8;
-        float4 wv[MAXG];
-        uint2 xb[TT][MAXG];
+    if (e >= E) return;
+    const int groups = H >> 8;
+    float4 wv[MAXG];
+    uint2 xb[TT][MAXG];
+#pragma unroll
+    for (int j = 0; j < MAXG; ++j)
+        if (j < groups)
+            wv[j] = *reinterpret_cast<const float4 *>(wr + (size_t)e * H + (j << 8) + (lane << 2));
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int j = 0; j < MAXG; ++j)
-            if (j < groups)
-                wv[j] = *reinterpret_cast<const float4 *>(wr + (size_t)e * H + (j << 8) + (lane << 2));
+            if (j < groups && t0 + t < T)
+                xb[t][j] = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + t) * H + (j << 8) + (lane << 2));
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < TT; ++t) {
+        if (t0 + t >= T) break;
+        float a = 0.0f;
 #pragma unroll
-            for (int j = 0; j < MAXG; ++j)
-                if (j < groups && t0 + t < T)
-                    xb[t][j] = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + t) * H + (j << 8) + (lane << 2));
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            if (t0 + t >= T) break;
-            float a = 0.0f;
-#pragma unroll
-            for (int j = 0; j < MAXG; ++j) {
-                if (j < groups) {
-                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].x & 0xFFFFu), wv[j].x, a);
-                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].x >> 16), wv[j].y, a);
-                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].y & 0xFFFFu), wv[j].z, a);
-                    a = __builtin_fmaf(bf16_to_f32(xb[t][j].y >> 16), wv[j].w, a);
-                }
+        for (int j = 0; j < MAXG; ++j) {
+            if (j < groups) {
+                a = __builtin_fmaf(bf16_to_f32(xb[t][j].x & 0xFFFFu), wv[j].x, a);
+                a = __builtin_fmaf(bf16_to_f32(xb[t][j].x >> 16), wv[j].y, a);
+                a = __builtin_fmaf(bf16_to_f32(xb[t][j].y & 0xFFFFu), wv[j].z, a);
+                a = __builtin_fmaf(bf16_to_f32(xb[t][j].y >> 16), wv[j].w, a);
             }
-            a = wave_sum_xor(a, 1);
-            if (lane == 0) logits[(size_t)(t0 + t) * E + e] = a;
         }
+        a = wave_sum_xor(a, 1);
+        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = a;
     }
-    // last block to arrive does the routing
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(arrivals, 1u);
-        s_last = (prev == gridDim.x * gridDim.y - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (threadIdx.x == 0) *arrivals = 0u;
-    route_block(logits, T, E, K, idx_out, w_out, counts, offsets, active, perm, inv);
 }
 
 template <int TT>
-static void router_route_launch(const Shape &s, dim3 grid, hipStream_t st, const uint16_t *x,
-                                const float *wr, int T, const Workspace &ws) {
+static void router_small_launch(const Shape &s, dim3 grid, hipStream_t st, const uint16_t *x,
+                                const float *wr, int T, float *logits) {
     const int g = s.H / 256;
-#define BQ_RR(G)                                                                               \
-    router_route_small_kernel<TT, G><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, s.K, ws.logits, \
-                                                           ws.arrivals, ws.idx, ws.w, ws.counts, \
-                                                           ws.offsets, ws.active, ws.perm, ws.inv)
-    if (g <= 1) BQ_RR(1);
-    else if (g <= 4) BQ_RR(4);
-    else if (g <= 16) BQ_RR(16);
-    else BQ_RR(32);
-#undef BQ_RR
-}
-
-__global__ void zero_u32_kernel(uint32_t *p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
-hipError_t launch_zero_arrivals(const Workspace &ws, hipStream_t st) {
-    zero_u32_kernel<<<1, 64, 0, st>>>(ws.arrivals, 1);
-    return hipGetLastError();
+    if (g <= 1) router_small_kernel<TT, 1><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else if (g <= 4) router_small_kernel<TT, 4><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else if (g <= 16) router_small_kernel<TT, 16><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else router_small_kernel<TT, 32><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
 }
 
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
                                      const Workspace &ws, hipStream_t st) {
     if (T < 1 || T > kDecodeMaxTokens || s.H / 256 > 32) return hipErrorInvalidValue;
     if (T == 1)
-        router_route_launch<1>(s, dim3(1, (s.E + 3) / 4), st, x, wr, T, ws);
+        router_small_launch<1>(s, dim3(1, (s.E + 3) / 4), st, x, wr, T, ws.logits);
     else
-        router_route_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws);
+        router_small_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws.logits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    route_small_kernel<<<1, kRouteThreads, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
+                                                    ws.counts, ws.offsets, ws.active, ws.perm,
+                                                    ws.inv);
     return hipGetLastError();
 }
 

@@ -105,9 +105,7 @@ int moe_workspace_size(const moe_layer_desc *desc, size_t *bytes);
 
 /* Validate desc and bind a caller-owned device workspace (256-byte aligned,
  * at least moe_workspace_size bytes, kept alive until moe_layer_destroy).
- * Writes a new handle to *out.  Makes no device call (the first decode-path
- * forward on a handle enqueues one small kernel that zeroes a counter in the
- * workspace). */
+ * Writes a new handle to *out.  Makes no device call. */
 int moe_layer_create(const moe_layer_desc *desc, void *workspace, size_t ws_bytes,
                      moe_layer **out);
 
@@ -170,21 +168,21 @@ int moe_layer_set_profiling(moe_layer *layer, int32_t slots);
  * moe_layer_set_profiling. */
 int moe_layer_profile_read(moe_layer *layer, float *ms, int32_t slots);
 
-/* Measurement aid: enqueue the kernels of one stage of the last forward
- * (MOE_STAGE_GATEUP or MOE_STAGE_DOWN) `reps` times back to back on
- * hip_stream, reusing that forward's routing, so that events around the call
- * time the stage's kernels alone.  Repetition i reads the layer at
- * packed_experts + (i % n_copies) * copy_stride (cycling through copies keeps
- * the weights from being served by the last-level cache); x_bf16 and out are
- * the last forward's token rows and output ([T][hidden], same alignment rules
- * as moe_layer_forward; out is only written by the decode down stage).  The
- * stage's results are those of the last forward again.  Returns MOE_EINVAL
- * before the first forward, for another stage, reps < 1, n_copies < 1,
- * a copy_stride not a multiple of 16, or a bad pointer; MOE_EHIP if a launch
- * fails. */
+/* Measurement aid: enqueue the kernels of one stage (MOE_STAGE_*) of the
+ * last forward `reps` times back to back on hip_stream, with that forward's
+ * inputs, so that events around the call time the stage's kernels alone.
+ * Repetition i reads the layer at packed_experts + (i % n_copies) *
+ * copy_stride (cycling through copies keeps the weights from being served by
+ * the last-level cache); x_bf16, router_w and out are the last forward's
+ * arguments (same alignment rules as moe_layer_forward).  Every stage
+ * recomputes exactly what the forward computed, so replaying a stage leaves
+ * the workspace and out as the forward left them.  Returns MOE_EINVAL before
+ * the first forward, for a stage the last forward's path does not run,
+ * reps < 1, n_copies < 1, a copy_stride not a multiple of 16, or a bad
+ * pointer; MOE_EHIP if a launch fails. */
 int moe_layer_replay_stage(moe_layer *layer, int32_t stage, int32_t reps, const void *x_bf16,
-                           const void *packed_experts, size_t copy_stride, int32_t n_copies,
-                           float *out, void *hip_stream);
+                           const float *router_w, const void *packed_experts, size_t copy_stride,
+                           int32_t n_copies, float *out, void *hip_stream);
 
 /* Release the handle (not the workspace).  NULL is a no-op. */
 void moe_layer_destroy(moe_layer *layer);

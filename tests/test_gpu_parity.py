@@ -165,8 +165,7 @@ def test_mimo_prefill_2048(torch_dev):
 @pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
 def test_replay_stage_reproduces_forward(torch_dev, path):
     """moe_layer_replay_stage re-runs a stage of the last forward: replaying
-    gate/up and down (and, for large batches, re-running the combine through a
-    second forward) leaves the output bit-identical."""
+    every stage of the path, in order, leaves the output bit-identical."""
     from gpu_harness import Runner
     import bit_quantized_moe_gemv_amd as bq
     torch = torch_dev
@@ -178,13 +177,15 @@ def test_replay_stage_reproduces_forward(torch_dev, path):
     out = torch.from_numpy(ref.astype(np.float32)).cuda()
     st = torch.cuda.current_stream().cuda_stream
     layer = run.layer
-    run.layer.forward(xd, torch.from_numpy(wr).cuda(), run.packed, out=out)
-    for stage in ("gateup", "down"):
-        rc = layer.replay_stage_raw(stage, 3, int(xd.data_ptr()), int(run.packed.data_ptr()),
-                                    0, 1, int(out.data_ptr()), st)
-        assert rc == bq.MOE_OK
+    wd = torch.from_numpy(wr).cuda()
+    run.layer.forward(xd, wd, run.packed, out=out)
+    stages = (("router", "gateup", "down") if path == DEC else
+              ("router", "select", "permute", "gateup", "down", "combine"))
+    args = (int(xd.data_ptr()), int(wd.data_ptr()), int(run.packed.data_ptr()), 0, 1,
+            int(out.data_ptr()), st)
+    for stage in stages:
+        assert layer.replay_stage_raw(stage, 3, *args) == bq.MOE_OK
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
-    bad = layer.replay_stage_raw("router", 1, int(xd.data_ptr()), int(run.packed.data_ptr()),
-                                 0, 1, int(out.data_ptr()), st)
-    assert bad == bq.MOE_EINVAL
+    if path == DEC:
+        assert layer.replay_stage_raw("combine", 1, *args) == bq.MOE_EINVAL
