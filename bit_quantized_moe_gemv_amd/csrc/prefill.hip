@@ -269,66 +269,180 @@ struct PrefillLds {
 };
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Grid: E * ceil(I/256) * 2 blocks.  Block (b, half th)
-// owns gate row groups 16b..16b+15 and their up partners (I/16 + 16b ..), and
-// the expert's tokens in 64-token chunks th, th+2, ...; wave w computes gate
-// groups 16b+4w..+3 and their 4 up partners.  The two halves of a slice are
-// neighbouring blocks on one XCD and fetch its weights from HBM about once.
-// Groups past the end (I not a multiple of 256) are clamped to valid data and
-// never stored.
+// gate/up + SwiGLU.  Grid: E * I/128 * 2 blocks of 4 waves; two blocks share
+// a CU (51 KiB of LDS and at most 256 registers per wave each), so every SIMD
+// runs two independent waves that hide each other's stalls.  Block (b, half
+// th) of expert e owns gate row groups 8b..8b+7 and their up partners and the
+// expert's tokens in 64-token chunks th, th+2, ...; wave w computes gate
+// groups 8b+2w, +1 and their up partners.  The two halves of a slice are
+// neighbouring blocks on one XCD, so the second one's weights mostly come
+// from that XCD's L2.  Per 128-column step every wave issues its four 1 KiB
+// pieces of the B stage, the scales of its 4 groups, then its 4 code loads,
+// kGuRing-1 steps ahead, branch-free so the wait counts stay exact.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPfThreads) void prefill_gateup_mxfp4(
+constexpr int kGuWaves = 4;
+constexpr int kGuThreads = kGuWaves * 64;
+constexpr int kGuGroups = 4;  // row groups per wave
+constexpr int kGuRing = 3;
+
+// B stage of one 128-column step: [chunk group cg][token m][4 x 16 B], the
+// 16-byte chunk c = 4cg + p (columns 8c..8c+7) of token m kept at position
+// p ^ ((m/4) % 4).  A copy instruction moves 64 contiguous bytes of each of 16
+// token rows (lane l: token 16w + l/4, position l%4), and the MFMA reads of
+// 16 tokens touch 16 distinct bank groups.
+// Scales: each wave copies those of its own 4 groups (4 replicas of 256 B:
+// [replica][group][tile q][row]), so every wave issues the same loads per step.
+struct GuLds {
+    uint8_t b[kGuRing][4][64][64];          // 16 KiB per slot
+    uint8_t sc[kGuRing][kGuWaves][4][256];  // 4 KiB per slot
+};
+
+// MFMAs of one step for one wave: 4 K steps x 4 groups x mt token tiles.  The
+// next K step's B operands and dequantised A operands are prepared before the
+// current K step's MFMAs (double buffering).  Every step dequantises, even
+// with no token tile, so no load is left in flight on a ring register.
+__device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const GuLds &lds,
+                                        int slot, int wave, int mt, int lane,
+                                        f32x4 (&acc)[kGuGroups][4]) {
+    const int q = lane >> 4, n = lane & 15;
+    float scale[kGuGroups];
+#pragma unroll
+    for (int g = 0; g < kGuGroups; ++g)
+        scale[g] = e8m0_to_f32(lds.sc[slot][wave][0][64 * g + 16 * q + n]);
+    bf16x8 a[2][kGuGroups];
+    bf16x8 bv[2][4];
+    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            bv[buf][t] = *reinterpret_cast<const bf16x8 *>(
+                &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
+    };
+    auto dequant = [&](int buf, int ks) {
+#pragma unroll
+        for (int g = 0; g < kGuGroups; ++g) {
+            const uint4 c = code[g];
+            const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
+            a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
+        }
+    };
+    load_b(0, 0);
+    dequant(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1;
+        if (ks < 3) {
+            load_b(cur ^ 1, ks + 1);
+            dequant(cur ^ 1, ks + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < mt) {
+#pragma unroll
+                for (int g = 0; g < kGuGroups; ++g)
+                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][t], acc[g][t]);
+            }
+    }
+}
+
+__device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
+                                            int nsuper, const int (&grp)[kGuGroups], int sgrp,
+                                            GuLds &lds, const uint16_t *brow, int wave, int lane,
+                                            int mt, f32x4 (&acc)[kGuGroups][4]) {
+    constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
+    uint4 ring[kGuRing][kGuGroups];
+    uint32_t goff[kGuGroups];
+#pragma unroll
+    for (int g = 0; g < kGuGroups; ++g)
+        goff[g] = (uint32_t)((size_t)grp[g] * kt * 256) + lane * 16;
+    auto issue = [&](int slot, int J) {
+        // B: copy i of this wave moves chunk group i of tokens 16w..16w+15;
+        // lane l (token 16w + l/4) fills position l%4
+        const int swz = (lane & 3) ^ ((lane >> 4) & 3);  // chunk within the group
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            copy_lds16(brow + 128 * J + 8 * (4 * i + swz), lds.b[slot][i][16 * wave]);
+        // scales: lane l copies group (l/4)%4 (row group sgrp), tile 4J + l%4
+        copy_lds16(scales + ((size_t)sgrp * kt + 4 * J + (lane & 3)) * 16, lds.sc[slot][wave][0]);
+#pragma unroll
+        for (int g = 0; g < kGuGroups; ++g)
+            ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
+    };
+    const int last = nsuper - 1;
+#pragma unroll
+    for (int j = 0; j < kGuRing - 1; ++j) issue(j, min(j, last));
+    for (int J0 = 0; J0 < nsuper; J0 += kGuRing) {
+#pragma unroll
+        for (int jj = 0; jj < kGuRing; ++jj) {
+            const int J = J0 + jj;
+            wait_vmcnt<(kGuRing - 2) * C>();  // step J has landed
+            stage_barrier();
+            issue((jj + kGuRing - 1) % kGuRing, min(J + kGuRing - 1, last));
+            if (J < nsuper) gu_step(ring[jj], lds, jj, wave, mt, lane, acc);
+        }
+    }
+    wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
+}
+
+__global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
     int H, int I, int K, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo) {
-    __shared__ __align__(16) PrefillLds lds;
+    __shared__ __align__(16) GuLds lds;
     int e, part;
-    map_expert_block(blockIdx.x, E, ((I + 255) / 256) * 2, &e, &part);
-    const int blk = part >> 1, th = part & 1;
+    map_expert_block(blockIdx.x, E, (I / 128) * 2, &e, &part);
+    const int b = part >> 1, th = part & 1;
     const int p0 = offsets[e];
     const int ne = offsets[e + 1] - p0;
     if (64 * th >= ne) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
     const int ngate = I / 16;
     const uint8_t *ex = packed + (size_t)e * expert_bytes;
-    const BlockGroups bg{0, blk, ngate};
+    const size_t kt = (size_t)(H / 32);
+    int grp[kGuGroups];
+#pragma unroll
+    for (int g = 0; g < kGuGroups; ++g) grp[g] = (g < 2 ? 0 : ngate) + 8 * b + 2 * wave + (g & 1);
+    // the scale copy's lane l covers the wave's group (l/4)%4
+    const int sg = (lane >> 2) & 3;
+    const int sgrp = (sg < 2 ? 0 : ngate) + 8 * b + 2 * wave + (sg & 1);
 
     for (int c0 = 64 * th; c0 < ne; c0 += 128) {
         const int nt = min(64, ne - c0);
-        const uint16_t *row = x + (size_t)(perm[p0 + c0 + min(lane, nt - 1)] / K) * H;
-        f32x4 acc[kPfGroups][4];
+        const int mt = (nt + 15) / 16;
+        // the token row this lane copies: token 16w + l/4 of the chunk
+        const uint16_t *brow =
+            x + (size_t)(perm[p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)] / K) * H;
+        f32x4 acc[kGuGroups][4];
 #pragma unroll
-        for (int g = 0; g < kPfGroups; ++g)
+        for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 64 * th) stage_barrier();  // previous chunk's readers are done with the rings
-        run_pipeline<1>(ex, ex + (size_t)I * H, (size_t)(H / 32), H / 128, bg, 0, lds.b, lds.sc,
-                        row, row, wave, lane, acc);
-        // epilogue: lane holds rows 4q..4q+3 of each group for token 16t+n;
-        // gate group i pairs with up group 4+i
+        gu_pipeline(ex, ex + (size_t)I * H, kt, H / 128, grp, sgrp, lds, brow, wave, lane, mt,
+                    acc);
+        // epilogue: lane holds rows 4q..4q+3 of each group for token 16t + n;
+        // gate group i pairs with up group 2 + i
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int m = 16 * t + n;
             if (m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int gg = 16 * blk + 4 * wave + i;  // gate group
-                    if (gg < ngate) {
-                        uint32_t hi[4], lo[4];
+                for (int i = 0; i < 2; ++i) {
+                    const int gg = 8 * b + 2 * wave + i;  // gate group
+                    uint32_t hi[4], lo[4];
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const float hv = silu_f32(acc[i][t][jj]) * acc[4 + i][t][jj];
-                            hi[jj] = f32_to_bf16_rne(hv);
-                            lo[jj] = f32_to_bf16_rne(hv - bf16_to_f32(hi[jj]));
-                        }
-                        const size_t col = (size_t)16 * gg + 4 * q;
-                        *reinterpret_cast<uint2 *>(h_hi + p * I + col) =
-                            make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-                        *reinterpret_cast<uint2 *>(h_lo + p * I + col) =
-                            make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float hv = silu_f32(acc[i][t][jj]) * acc[2 + i][t][jj];
+                        hi[jj] = f32_to_bf16_rne(hv);
+                        lo[jj] = f32_to_bf16_rne(hv - bf16_to_f32(hi[jj]));
                     }
+                    const size_t col = (size_t)16 * gg + 4 * q;
+                    *reinterpret_cast<uint2 *>(h_hi + p * I + col) =
+                        make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+                    *reinterpret_cast<uint2 *>(h_lo + p * I + col) =
+                        make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
                 }
             }
         }
@@ -389,7 +503,7 @@ hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const
                                  const Workspace &ws, hipStream_t st) {
     uint16_t *hh = static_cast<uint16_t *>(ws.h);
     uint16_t *hl = hh + (size_t)T * s.K * s.I;
-    prefill_gateup_mxfp4<<<s.E * ((s.I + 255) / 256) * 2, kPfThreads, 0, st>>>(
+    prefill_gateup_mxfp4<<<s.E * (s.I / 128) * 2, kGuThreads, 0, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, hh, hl);
     return hipGetLastError();
 }
