@@ -5,28 +5,28 @@
 // The micro-batch matters (a 512-token micro-batch leaves much of prefill
 // unused because each of the 256 experts then sees too few tokens per matmul
 // -- TrevorJS GGUF card, "Speed"): a block owns one slice of one expert's
-// weights and multiplies it with every token routed to that expert, so the
-// weights leave HBM once.
+// weights and multiplies it with the expert's tokens, 64 at a time.
 //
-// Pipeline of a block (four waves, one per SIMD, one block per CU): the
-// kernel is bound by streaming weights from HBM, so what matters is the number
-// of weight bytes in flight.  Each step (one K super-step of 128 columns) every
-// wave issues, in a fixed order, its share of the B operand stage and of the
-// scales (global_load_lds straight into a 4-deep LDS ring) and then its own 8
-// row groups of packed code tiles (1 KiB wave loads into a 4-deep register
-// ring).  Because a wave's load counter completes in issue order, waiting
-// until no more than "the loads of the steps after J" are outstanding means
-// step J has landed; one barrier then publishes the B stage.  Waves are wide
-// (8 row groups x 128 tokens, 256 fp32 accumulators in AGPRs, using the
-// 512-register budget of one wave per SIMD) so that a step's MFMA work covers
-// the memory latency three steps deep.  Weights are dequantised to bf16 in
-// registers (every E2M1 value times an in-range E8M0 scale is a bf16 value, so
-// the A operand and the products are exact) and accumulated in fp32.
+// Shape of a kernel: blocks of four waves with 4 row groups (16 weight rows
+// each) per wave, at most 256 registers and about 60-72 KiB of LDS per block,
+// so two independent blocks share each CU and every SIMD runs two waves that
+// hide each other's memory and barrier stalls.  Per K step of 128 columns each
+// wave issues, in a fixed order, its copies of the B stage and of its groups'
+// scales (global_load_lds into an LDS ring) and its 4 code loads (1 KiB wave
+// loads into a register ring), a fixed number of steps ahead.  Loads are
+// issued unconditionally (past the end they repeat the last step's
+// addresses) so the wait counts are compile-time constants that the compiler
+// tracks exactly; a conditional issue makes it wait for every load in flight.
+//
+// Weights are dequantised to bf16 in registers: every E2M1 value times an
+// in-range E8M0 scale is a bf16 value, so the A operand and the products are
+// exact, and the dequantisation of K step s+1 runs while the MFMAs of step s
+// issue.
 //
 // MFMA roles: A = 16 weight rows x 32 K (lane l: row l%16, K slice
 // 8*(l/16)..+7), B = 32 K x 16 tokens, D[row][token].  Lane (n, q) of a wave
 // holds the 16 code bytes of tile column 4J+q of its row n: K columns
-// 128J+32q .. +31; MFMA step s uses bytes 4s..4s+3 (columns 128J+32q+8s..+7),
+// 128J+32q .. +31; K step s uses bytes 4s..4s+3 (columns 128J+32q+8s..+7),
 // and the B operand of lane (m, q) at step s is x[m][128J+32q+8s..+7].
 //
 // SwiGLU is fused into the gate/up epilogue in fp32.  Expert intermediates
@@ -37,23 +37,6 @@
 #include "moe_internal.h"
 
 namespace bqmoe {
-
-constexpr int kPfWaves = 4;    // one per SIMD; each owns 8 weight row groups
-constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfRing = 3;     // steps in flight (register code ring, LDS B ring)
-constexpr int kPfGroups = 8;   // row groups per wave
-constexpr int kPfBlockGroups = kPfWaves * kPfGroups;
-
-// B operand stage: [s][q][m][8 bf16] for a 128-column super-step, m = token.
-template <int TOK>
-struct BStage {
-    uint8_t b[4][4][TOK][16];
-};
-
-// Scales of a block's 32 row groups for one super-step: [group][tile q][row n].
-struct ScaleStage {
-    uint8_t s[kPfBlockGroups][64];
-};
 
 // Wait until at most N vector-memory loads of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, other counters open).
@@ -96,181 +79,9 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// This wave's copies into one B stage (64 tokens): (s, q) slices wave,
-// wave+4, wave+8, wave+12, 1 KiB each.  row: the lane's token row (element
-// pointer into a [*, K] bf16 matrix).
-__device__ __forceinline__ void load_bstage(BStage<64> *dst, const uint16_t *row, int J, int wave) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = wave + 4 * i;
-        const int s = c >> 2, q = c & 3;
-        copy_lds16(row + 128 * J + 32 * q + 8 * s, dst->b[s][q][0]);
-    }
-}
-
-// Row groups of a block.  A block owns 32 row groups; group index i of the
-// block maps to a row group of the matrix through BlockGroups::at(i).
-struct BlockGroups {
-    int mode;   // 0: gate/up (i < 16 gate 16b+i, else up partner), 1: down (32b+i)
-    int blk;
-    int limit;  // gate groups (mode 0) or row groups (mode 1)
-    __device__ __forceinline__ int at(int i) const {
-        if (mode == 0) {
-            const int g = min(16 * blk + (i & 15), limit - 1);
-            return i < 16 ? g : limit + g;
-        }
-        return min(32 * blk + i, limit - 1);
-    }
-};
-
-// Block group index of the wave's group g: gate/up waves take gate 4w..4w+3
-// and their up partners 16+4w..; down waves take 8w..8w+7.
-__device__ __forceinline__ int wave_group(int mode, int wave, int g) {
-    return mode == 0 ? (g < 4 ? 4 * wave + g : 16 + 4 * wave + (g - 4)) : 8 * wave + g;
-}
-
-// Scales of step J for the block's 32 groups: waves 0 and 1 copy 16 groups each
-// (lane l: block group 16*wave + l/4, tile 4J + l%4).
-__device__ __forceinline__ void load_scales(ScaleStage *dst, const uint8_t *scales,
-                                            const BlockGroups &bg, size_t kt, int J, int wave,
-                                            int lane) {
-    const int g = bg.at(16 * wave + (lane >> 2));
-    copy_lds16(scales + ((size_t)g * kt + 4 * J + (lane & 3)) * 16, dst->s[16 * wave]);
-}
-
-// MFMAs of one super-step for a wave: 4 K steps x 8 row groups x 4 token
-// tiles; NB B operands per tile (1: x, 2: h hi and lo).  Operands are double
-// buffered: while the MFMAs of K step s run, the wave reads step s+1's B
-// operands from LDS and dequantises its A operands, interleaved one VALU op
-// per MFMA (or per two for NB = 2) so the matrix core never waits for them.
-// Token tiles past the chunk's tokens multiply clamped duplicate rows whose
-// results are never stored; a branch per tile would expose an LDS round trip.
-template <int NB>
-__device__ __forceinline__ void mfma_step(const uint4 (&code)[kPfGroups], const ScaleStage *sc,
-                                          const BStage<64> *b0, const BStage<64> *b1, int mode,
-                                          int wave, int lane, f32x4 (&acc)[kPfGroups][4]) {
-    const int q = lane >> 4, n = lane & 15;
-    float scale[kPfGroups];
-#pragma unroll
-    for (int g = 0; g < kPfGroups; ++g)
-        scale[g] = e8m0_to_f32(sc->s[wave_group(mode, wave, g)][q * 16 + n]);
-    bf16x8 a[2][kPfGroups];
-    bf16x8 bv[2][NB][4];
-    auto load_b = [&](int buf, int s) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            bv[buf][0][t] = *reinterpret_cast<const bf16x8 *>(b0->b[s][q][16 * t + n]);
-            if (NB == 2) bv[buf][NB - 1][t] = *reinterpret_cast<const bf16x8 *>(b1->b[s][q][16 * t + n]);
-        }
-    };
-    auto dequant = [&](int buf, int s) {
-#pragma unroll
-        for (int g = 0; g < kPfGroups; ++g) {
-            const uint4 c = code[g];
-            const uint32_t d = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
-            a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
-        }
-    };
-    load_b(0, 0);
-    dequant(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int cur = s & 1;
-        if (s < 3) {
-            load_b(cur ^ 1, s + 1);
-            dequant(cur ^ 1, s + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int g = 0; g < kPfGroups; ++g)
-                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][nb][t], acc[g][t]);
-        if (s < 3) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * NB, 0);  // LDS reads first
-#pragma unroll
-            for (int i = 0; i < 4 * kPfGroups; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // dequant op
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// The pipeline: per step J, every wave issues [its B copies, its scale copy
-// (waves 0-1), its 8 code loads]; steps run kPfRing-1 ahead.  C = loads per
-// step of this wave, NB = B operands per step (1: x, 2: h hi and lo).
-//
-// The loop is branch-free around loads: past the last step the issue repeats
-// the last step's addresses (cache hits, never consumed), so every wave always
-// has exactly kPfRing-1 steps in flight at a wait and the compiler's own
-// load-counter tracking stays exact.  A conditional issue makes it fall back
-// to waiting for every load in flight, which serialises the stream.
-template <int C, int NB>
-__device__ __forceinline__ void pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
-                                         int nsuper, const BlockGroups &bg, int mode,
-                                         BStage<64> (*bring)[2], ScaleStage *scring,
-                                         const uint16_t *row0, const uint16_t *row1,
-                                         int wave, int lane, f32x4 (&acc)[kPfGroups][4]) {
-    uint4 ring[kPfRing][kPfGroups];
-    uint32_t goff[kPfGroups];  // byte offset of the wave's group g, tile 0, this lane
-#pragma unroll
-    for (int g = 0; g < kPfGroups; ++g)
-        goff[g] = (uint32_t)((size_t)bg.at(wave_group(mode, wave, g)) * kt * 256) + lane * 16;
-    auto issue = [&](int slot, int J) {
-        load_bstage(&bring[slot][0], row0, J, wave);
-        if (NB == 2) load_bstage(&bring[slot][1], row1, J, wave);
-        if (wave < 2) load_scales(&scring[slot], scales, bg, kt, J, wave, lane);
-#pragma unroll
-        for (int g = 0; g < kPfGroups; ++g)
-            ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
-    };
-    const int last = nsuper - 1;
-#pragma unroll
-    for (int j = 0; j < kPfRing - 1; ++j) issue(j, min(j, last));
-    for (int J0 = 0; J0 < nsuper; J0 += kPfRing) {
-#pragma unroll
-        for (int jj = 0; jj < kPfRing; ++jj) {
-            const int J = J0 + jj;
-            wait_vmcnt<(kPfRing - 2) * C>();  // step J has landed
-            stage_barrier();
-            issue((jj + kPfRing - 1) % kPfRing, min(J + kPfRing - 1, last));
-            if (J < nsuper)
-                mfma_step<NB>(ring[jj], &scring[jj], &bring[jj][0], &bring[jj][1], mode, wave,
-                              lane, acc);
-        }
-    }
-    wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
-}
-
-// Dispatch on the per-step load count of this wave (compile-time wait counts).
-template <int NB>
-__device__ __forceinline__ void run_pipeline(const uint8_t *codes, const uint8_t *scales,
-                                             size_t kt, int nsuper, const BlockGroups &bg,
-                                             int mode, BStage<64> (*bring)[2],
-                                             ScaleStage *scring, const uint16_t *row0,
-                                             const uint16_t *row1, int wave, int lane,
-                                             f32x4 (&acc)[kPfGroups][4]) {
-    constexpr int CB = 4 * NB;  // B copies per step
-    if (wave < 2)
-        pipeline<CB + 1 + kPfGroups, NB>(codes, scales, kt, nsuper, bg, mode, bring, scring, row0,
-                                         row1, wave, lane, acc);
-    else
-        pipeline<CB + kPfGroups, NB>(codes, scales, kt, nsuper, bg, mode, bring, scring, row0,
-                                     row1, wave, lane, acc);
-}
-
-struct PrefillLds {
-    BStage<64> b[kPfRing][2];  // x (slot 0) or h hi, lo: up to 128 KiB
-    ScaleStage sc[kPfRing];    // 8 KiB
-};
-
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  Grid: E * I/128 * 2 blocks of 4 waves; two blocks share
-// a CU (51 KiB of LDS and at most 256 registers per wave each), so every SIMD
+// a CU (60 KiB of LDS and at most 256 registers per wave each), so every SIMD
 // runs two independent waves that hide each other's stalls.  Block (b, half
 // th) of expert e owns gate row groups 8b..8b+7 and their up partners and the
 // expert's tokens in 64-token chunks th, th+2, ...; wave w computes gate
@@ -450,50 +261,152 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
 }
 
 // ---------------------------------------------------------------------------
-// down.  Grid: E * ceil(H/512) * 2 blocks.  Block (b, half th) owns output row
-// groups 32b..32b+31 (wave w: groups 32b+8w..+7) and the expert's tokens in
-// 64-token chunks th, th+2, ...; h rows are contiguous (route-position order).
+// down.  Grid: E * H/256 * 2 blocks of 4 waves, two blocks per CU as in
+// gate/up.  Block (b, half th) owns output row groups 16b..16b+15 (wave w:
+// 16b+4w..+3) and the expert's tokens in 64-token chunks th, th+2, ...; the h
+// rows are contiguous (route-position order), hi and lo halves run through
+// the MFMA into the same accumulators.  The B stage of a step holds both
+// halves (32 KiB), so the ring is 2 deep: a step's loads are issued one step
+// ahead and waited for at the next step.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPfThreads) void prefill_down_mxfp4(
+constexpr int kDnPfWaves = 4;
+constexpr int kDnPfThreads = kDnPfWaves * 64;
+constexpr int kDnPfGroups = 4;
+constexpr int kDnPfRing = 2;
+
+struct DnLds {
+    uint8_t b[kDnPfRing][2][4][64][64];           // [slot][hi, lo][chunk group][token][64 B]
+    uint8_t sc[kDnPfRing][kDnPfWaves][4][256];    // [slot][wave][replica][group, tile, row]
+};
+
+__device__ __forceinline__ void dn_step(const uint4 (&code)[kDnPfGroups], const DnLds &lds,
+                                        int slot, int wave, int mt, int lane,
+                                        f32x4 (&acc)[kDnPfGroups][4]) {
+    const int q = lane >> 4, n = lane & 15;
+    float scale[kDnPfGroups];
+#pragma unroll
+    for (int g = 0; g < kDnPfGroups; ++g)
+        scale[g] = e8m0_to_f32(lds.sc[slot][wave][0][64 * g + 16 * q + n]);
+    bf16x8 a[2][kDnPfGroups];
+    bf16x8 bv[2][2][4];
+    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks, both halves
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                bv[buf][hl][t] = *reinterpret_cast<const bf16x8 *>(
+                    &lds.b[slot][hl][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
+    };
+    auto dequant = [&](int buf, int ks) {
+#pragma unroll
+        for (int g = 0; g < kDnPfGroups; ++g) {
+            const uint4 c = code[g];
+            const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
+            a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
+        }
+    };
+    load_b(0, 0);
+    dequant(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1;
+        if (ks < 3) {
+            load_b(cur ^ 1, ks + 1);
+            dequant(cur ^ 1, ks + 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < mt) {
+#pragma unroll
+                for (int g = 0; g < kDnPfGroups; ++g) {
+                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][0][t], acc[g][t]);
+                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][1][t], acc[g][t]);
+                }
+            }
+    }
+}
+
+__device__ __forceinline__ void dn_pipeline(const uint8_t *codes, const uint8_t *scales,
+                                            size_t kt, int nsuper, const int (&grp)[kDnPfGroups],
+                                            int sgrp, DnLds &lds, const uint16_t *rhi,
+                                            const uint16_t *rlo, int wave, int lane, int mt,
+                                            f32x4 (&acc)[kDnPfGroups][4]) {
+    constexpr int C = 8 + 1 + kDnPfGroups;  // loads per wave per step
+    static_assert(C < 16, "vmcnt range");
+    uint4 ring[kDnPfRing][kDnPfGroups];
+    uint32_t goff[kDnPfGroups];
+#pragma unroll
+    for (int g = 0; g < kDnPfGroups; ++g)
+        goff[g] = (uint32_t)((size_t)grp[g] * kt * 256) + lane * 16;
+    const int swz = (lane & 3) ^ ((lane >> 4) & 3);
+    auto issue = [&](int slot, int J) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            copy_lds16(rhi + 128 * J + 8 * (4 * i + swz), lds.b[slot][0][i][16 * wave]);
+            copy_lds16(rlo + 128 * J + 8 * (4 * i + swz), lds.b[slot][1][i][16 * wave]);
+        }
+        copy_lds16(scales + ((size_t)sgrp * kt + 4 * J + (lane & 3)) * 16, lds.sc[slot][wave][0]);
+#pragma unroll
+        for (int g = 0; g < kDnPfGroups; ++g)
+            ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
+    };
+    const int last = nsuper - 1;
+    issue(0, 0);
+    for (int J0 = 0; J0 < nsuper; J0 += kDnPfRing) {
+#pragma unroll
+        for (int jj = 0; jj < kDnPfRing; ++jj) {
+            const int J = J0 + jj;
+            wait_vmcnt<(kDnPfRing - 2) * C>();  // step J has landed
+            stage_barrier();
+            issue((jj + kDnPfRing - 1) % kDnPfRing, min(J + kDnPfRing - 1, last));
+            if (J < nsuper) dn_step(ring[jj], lds, jj, wave, mt, lane, acc);
+        }
+    }
+    wait_vmcnt<0>();
+}
+
+__global__ __launch_bounds__(kDnPfThreads, 2) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
     const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h_hi,
     const uint16_t *__restrict__ h_lo, float *__restrict__ y) {
-    __shared__ __align__(16) PrefillLds lds;
-    const int nrow = H / 16;
+    __shared__ __align__(16) DnLds lds;
     int e, part;
-    map_expert_block(blockIdx.x, E, ((H + 511) / 512) * 2, &e, &part);
-    const int blk = part >> 1, th = part & 1;
+    map_expert_block(blockIdx.x, E, (H / 256) * 2, &e, &part);
+    const int b = part >> 1, th = part & 1;
     const int p0 = offsets[e];
     const int ne = offsets[e + 1] - p0;
     if (64 * th >= ne) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
     const uint8_t *codes = packed + (size_t)e * expert_bytes + (size_t)I * H + (size_t)I * H / 16;
-    const BlockGroups bg{1, blk, nrow};
+    const size_t kt = (size_t)(I / 32);
+    int grp[kDnPfGroups];
+#pragma unroll
+    for (int g = 0; g < kDnPfGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
+    const int sgrp = 16 * b + 4 * wave + ((lane >> 2) & 3);
 
     for (int c0 = 64 * th; c0 < ne; c0 += 128) {
         const int nt = min(64, ne - c0);
-        const size_t r = (size_t)(p0 + c0 + min(lane, nt - 1)) * I;
-        f32x4 acc[kPfGroups][4];
+        const int mt = (nt + 15) / 16;
+        const size_t r = (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
+        f32x4 acc[kDnPfGroups][4];
 #pragma unroll
-        for (int g = 0; g < kPfGroups; ++g)
+        for (int g = 0; g < kDnPfGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 64 * th) stage_barrier();
-        run_pipeline<2>(codes, codes + (size_t)H * I / 2, (size_t)(I / 32), I / 128, bg, 1, lds.b,
-                        lds.sc, h_hi + r, h_lo + r, wave, lane, acc);
+        dn_pipeline(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, sgrp, lds, h_hi + r,
+                    h_lo + r, wave, lane, mt, acc);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int m = 16 * t + n;
             if (m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
-                for (int g = 0; g < kPfGroups; ++g) {
-                    const int gg = 32 * blk + 8 * wave + g;
-                    if (gg < nrow)
-                        *reinterpret_cast<float4 *>(y + p * H + 16 * gg + 4 * q) =
-                            make_float4(acc[g][t][0], acc[g][t][1], acc[g][t][2], acc[g][t][3]);
-                }
+                for (int g = 0; g < kDnPfGroups; ++g)
+                    *reinterpret_cast<float4 *>(y + p * H + 16 * grp[g] + 4 * q) =
+                        make_float4(acc[g][t][0], acc[g][t][1], acc[g][t][2], acc[g][t][3]);
             }
         }
     }
@@ -512,7 +425,7 @@ hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, con
                                hipStream_t st) {
     const uint16_t *hh = static_cast<const uint16_t *>(ws.h);
     const uint16_t *hl = hh + (size_t)T * s.K * s.I;
-    prefill_down_mxfp4<<<s.E * ((s.H + 511) / 512) * 2, kPfThreads, 0, st>>>(
+    prefill_down_mxfp4<<<s.E * (s.H / 256) * 2, kDnPfThreads, 0, st>>>(
         packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, hh, hl, ws.y);
     return hipGetLastError();
 }
