@@ -95,57 +95,98 @@ __device__ void wave_topk(const float *__restrict__ l, int E, int K, int *idx, f
 }
 
 // ---------------------------------------------------------------------------
-// router logits: one wave computes a TT-token x TE-expert tile
+// router logits for large batches.  A block (4 waves) computes a 16-token x
+// 16-expert tile; wave w owns experts 4w..4w+3 of the tile.  Per 256-column
+// group the block stages the 16 token rows (8 KiB) in LDS once, instead of
+// every wave fetching them, and each wave streams its 4 weight rows; the
+// next group's loads are issued before the current group's FMAs.  Lane c
+// holds columns 4c..4c+3 of every group, so each logit keeps the summation
+// order described above.  Rows past T or E are clamped duplicates that are
+// never stored.
 // ---------------------------------------------------------------------------
-template <int TT, int TE>
+constexpr int kRtTok = 16;  // tokens per block
+constexpr int kRtExp = 4;   // experts per wave
+
 __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict__ x,
                                                      const float *__restrict__ wr, int T, int H,
                                                      int E, float *__restrict__ logits) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * TT;
-    const int e0 = (blockIdx.y * 4 + wave) * TE;
-    if (e0 >= E) return;
-    float acc[TT][TE];
+    __shared__ __align__(16) uint2 xs[2][kRtTok][64];  // [buffer][token][lane]: 16 KiB
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * kRtTok;
+    const int e0 = (blockIdx.y * 4 + wave) * kRtExp;
+    float acc[kRtTok][kRtExp];
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < kRtTok; ++t)
 #pragma unroll
-        for (int e = 0; e < TE; ++e) acc[t][e] = 0.0f;
-
-    const int groups = H >> 8;
-    for (int j = 0; j < groups; ++j) {
-        const int k0 = (j << 8) + (lane << 2);
-        float4 wv[TE];
+        for (int e = 0; e < kRtExp; ++e) acc[t][e] = 0.0f;
+    // element offsets (32-bit: H * max(T, E) stays far below 2^32 here)
+    const float *wbase = wr + (lane << 2);
+    uint32_t woff[kRtExp];
 #pragma unroll
-        for (int e = 0; e < TE; ++e)
-            wv[e] = (e0 + e < E) ? *reinterpret_cast<const float4 *>(wr + (size_t)(e0 + e) * H + k0)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = 0; e < kRtExp; ++e) woff[e] = (uint32_t)min(e0 + e, E - 1) * (uint32_t)H;
+    // x staging: thread (token i*4 + wave, lane) moves 8 bytes per group
+    const uint16_t *xbase = x + (lane << 2);
+    uint32_t xoff[kRtTok / 4];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            uint2 xb = make_uint2(0u, 0u);
-            if (t0 + t < T) xb = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + t) * H + k0);
-            const float x0 = bf16_to_f32(xb.x & 0xFFFFu), x1 = bf16_to_f32(xb.x >> 16);
-            const float x2 = bf16_to_f32(xb.y & 0xFFFFu), x3 = bf16_to_f32(xb.y >> 16);
+    for (int i = 0; i < kRtTok / 4; ++i) xoff[i] = (uint32_t)min(t0 + 4 * i + wave, T - 1) * (uint32_t)H;
+    float4 wv[2][kRtExp];
+    uint2 xn[kRtTok / 4];
+    auto load_x = [&](int j) {
 #pragma unroll
-            for (int e = 0; e < TE; ++e) {
+        for (int i = 0; i < kRtTok / 4; ++i) xn[i] = *reinterpret_cast<const uint2 *>(xbase + xoff[i] + (j << 8));
+    };
+    auto load_w = [&](int buf, int j) {
+#pragma unroll
+        for (int e = 0; e < kRtExp; ++e) wv[buf][e] = *reinterpret_cast<const float4 *>(wbase + woff[e] + (j << 8));
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kRtTok / 4; ++i) xs[buf][4 * i + wave][lane] = xn[i];
+    };
+    auto fma_group = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < kRtTok; ++t) {
+            const uint2 v = xs[buf][t][lane];
+            const float x0 = bf16_to_f32(v.x & 0xFFFFu), x1 = bf16_to_f32(v.x >> 16);
+            const float x2 = bf16_to_f32(v.y & 0xFFFFu), x3 = bf16_to_f32(v.y >> 16);
+#pragma unroll
+            for (int e = 0; e < kRtExp; ++e) {
                 float a = acc[t][e];
-                a = __builtin_fmaf(x0, wv[e].x, a);
-                a = __builtin_fmaf(x1, wv[e].y, a);
-                a = __builtin_fmaf(x2, wv[e].z, a);
-                a = __builtin_fmaf(x3, wv[e].w, a);
+                a = __builtin_fmaf(x0, wv[buf][e].x, a);
+                a = __builtin_fmaf(x1, wv[buf][e].y, a);
+                a = __builtin_fmaf(x2, wv[buf][e].z, a);
+                a = __builtin_fmaf(x3, wv[buf][e].w, a);
                 acc[t][e] = a;
             }
         }
+    };
+    const int groups = H >> 8;
+    load_x(0);
+    load_w(0, 0);
+    store_x(0);  // waits for the x loads only
+    lds_barrier();
+    for (int j = 0; j < groups; j += 2) {
+        // group j (buffer 0) while group j+1 loads; then group j+1 (buffer 1)
+        load_x(min(j + 1, groups - 1));
+        load_w(1, min(j + 1, groups - 1));
+        fma_group(0);
+        store_x(1);
+        lds_barrier();
+        load_x(min(j + 2, groups - 1));
+        load_w(0, min(j + 2, groups - 1));
+        if (j + 1 < groups) fma_group(1);
+        store_x(0);
+        lds_barrier();
     }
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < kRtTok; ++t)
 #pragma unroll
-        for (int e = 0; e < TE; ++e) acc[t][e] = wave_sum_xor(acc[t][e], 1);
+        for (int e = 0; e < kRtExp; ++e) acc[t][e] = wave_sum_xor(acc[t][e], 1);
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < kRtTok; ++t)
 #pragma unroll
-        for (int e = 0; e < TE; ++e)
-            if (lane == ((t * TE + e) & 63) && t0 + t < T && e0 + e < E)
+        for (int e = 0; e < kRtExp; ++e)
+            if (lane == ((t * kRtExp + e) & 63) && t0 + t < T && e0 + e < E)
                 logits[(size_t)(t0 + t) * E + e0 + e] = acc[t][e];
 }
 
@@ -295,8 +336,8 @@ hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const fl
 
 hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
                          hipStream_t st) {
-    dim3 grid((T + 7) / 8, (s.E + 31) / 32);
-    router_kernel<8, 8><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    dim3 grid((T + kRtTok - 1) / kRtTok, (s.E + 4 * kRtExp - 1) / (4 * kRtExp));
+    router_kernel<<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
     return hipGetLastError();
 }
 
