@@ -71,18 +71,80 @@ __device__ __forceinline__ void reg_fence(uint4 &v) {
 // LDS-only barrier, so the weight stream is never stalled by them.  h is
 // written in fp32, in route-position order.
 // ---------------------------------------------------------------------------
-template <int NJ, int TC>
+// With R1 (a single token) the block routes the token itself: wave 0 selects
+// the top-k of the router logits (the same one-wave selection as the routing
+// kernel), every block takes the slot-th selected expert in ascending order,
+// and block (0, 0) publishes the routing for the down kernel and
+// moe_layer_routing.  This replaces a separate routing launch.
+template <int NJ, int TC, bool R1>
 __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
-    int H, int I, int K, const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ perm, float *__restrict__ h) {
+    int H, int I, int E, int K, int32_t *__restrict__ active, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm, float *__restrict__ h, const float *__restrict__ logits,
+    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
+    int32_t *__restrict__ inv) {
     extern __shared__ __align__(16) uint16_t xs[];  // [TC][H]
     __shared__ float red[4][TC][16];
     const int slot = blockIdx.x;
-    if (slot >= active[0]) return;
-    const int e = active[1 + slot];
-    const int p0 = offsets[e];
-    const int ne = offsets[e + 1] - p0;
+    int e, p0, ne;
+    if (R1) {
+        __shared__ int s_e;
+        if (threadIdx.x < 64) {
+            int sel[kMaxTopK];
+            float wt[kMaxTopK];
+            wave_topk(logits, E, K, sel, wt);
+            const int ln = threadIdx.x;
+            // ascending rank of each selected expert = its route position
+            int pos[kMaxTopK];
+#pragma unroll
+            for (int s2 = 0; s2 < kMaxTopK; ++s2) {
+                pos[s2] = 0;
+#pragma unroll
+                for (int j = 0; j < kMaxTopK; ++j)
+                    if (s2 < K && j < K) pos[s2] += sel[j] < sel[s2];
+            }
+            int mine = sel[0];
+#pragma unroll
+            for (int s2 = 0; s2 < kMaxTopK; ++s2)
+                if (s2 < K && pos[s2] == slot) mine = sel[s2];
+            if (ln == 0) s_e = mine;
+            if (blockIdx.x == 0 && blockIdx.y == 0) {
+#pragma unroll
+                for (int s2 = 0; s2 < kMaxTopK; ++s2)
+                    if (s2 < K && ln == s2) {
+                        idx_out[s2] = sel[s2];
+                        w_out[s2] = wt[s2];
+                        perm[pos[s2]] = s2;
+                        inv[s2] = pos[s2];
+                        active[1 + pos[s2]] = sel[s2];
+                    }
+                if (ln == 0) {
+                    active[0] = K;
+                    offsets[E] = K;
+                }
+                for (int ee = ln; ee < E; ee += 64) {
+                    int c = 0, below = 0;
+#pragma unroll
+                    for (int j = 0; j < kMaxTopK; ++j)
+                        if (j < K) {
+                            c += sel[j] == ee;
+                            below += sel[j] < ee;
+                        }
+                    counts[ee] = c;
+                    offsets[ee] = below;
+                }
+            }
+        }
+        lds_barrier();
+        e = s_e;
+        p0 = slot;
+        ne = 1;
+    } else {
+        if (slot >= active[0]) return;
+        e = active[1 + slot];
+        p0 = offsets[e];
+        ne = offsets[e + 1] - p0;
+    }
     const int rg = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, q = lane >> 4;
@@ -105,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
         // so that they do not queue behind the vector loads
         int trow[TC];
 #pragma unroll
-        for (int r = 0; r < TC; ++r) trow[r] = perm[p0 + c0 + min(r, nt - 1)] / K;
+        for (int r = 0; r < TC; ++r) trow[r] = R1 ? 0 : perm[p0 + c0 + min(r, nt - 1)] / K;
         uint4 xv[XN];
 #pragma unroll
         for (int i = 0; i < XN; ++i) {
@@ -308,22 +370,22 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
     }
 }
 
-template <int NJ, int TC>
+template <int NJ, int TC, bool R1>
 static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
     const int slots = min(s.E, T * s.K);
     dim3 grid(slots, s.I / 16);
-    decode_gateup_mxfp4<NJ, TC><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
-        x, packed, s.expert_bytes, s.H, s.I, s.K, ws.active, ws.offsets, ws.perm,
-        static_cast<float *>(ws.h));
+    decode_gateup_mxfp4<NJ, TC, R1><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
+        x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.active, ws.offsets, ws.perm,
+        static_cast<float *>(ws.h), ws.logits, ws.idx, ws.w, ws.counts, ws.inv);
     return hipGetLastError();
 }
 
 template <int NJ>
 static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
                                    const uint8_t *packed, const Workspace &ws, hipStream_t st) {
-    return T == 1 ? gateup_launch<NJ, 1>(s, T, x, packed, ws, st)
-                  : gateup_launch<NJ, kDecTC>(s, T, x, packed, ws, st);
+    return T == 1 ? gateup_launch<NJ, 1, true>(s, T, x, packed, ws, st)
+                  : gateup_launch<NJ, kDecTC, false>(s, T, x, packed, ws, st);
 }
 
 bool decode_supported(const Shape &s) {

@@ -14,87 +14,6 @@
 namespace bqmoe {
 
 // ---------------------------------------------------------------------------
-// top-k of one token by one wave
-// ---------------------------------------------------------------------------
-
-// (value, index) key: a beats b if its value is larger, or equal with a lower
-// index.  Comparing floats makes -0 and +0 equal, so they tie to the index.
-__device__ __forceinline__ bool key_beats(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-
-// Selects the k best experts of `l` (E <= 256 logits) and their softmax
-// weights.  Every lane returns the same idx[]/w[]; lane l owns experts l,
-// l+64, l+128, l+192, sorted once by key.  Each round reduces the lanes' heads
-// to the wave maximum, then to the lowest expert index holding it (both
-// reductions are exact, so the winner does not depend on reduction order); the
-// winning lane pops its head.
-__device__ __forceinline__ void cswap(float &va, int &ia, float &vb, int &ib) {
-    // after the call (va, ia) beats or equals (vb, ib)
-    const bool sw = key_beats(vb, ib, va, ia);
-    const float tv = sw ? vb : va;
-    const int ti = sw ? ib : ia;
-    vb = sw ? va : vb;
-    ib = sw ? ia : ib;
-    va = tv;
-    ia = ti;
-}
-
-__device__ void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
-    const int lane = threadIdx.x & 63;
-    float v0, v1, v2, v3;
-    int i0 = lane, i1 = lane + 64, i2 = lane + 128, i3 = lane + 192;
-    v0 = (i0 < E) ? l[i0] : -INFINITY;
-    v1 = (i1 < E) ? l[i1] : -INFINITY;
-    v2 = (i2 < E) ? l[i2] : -INFINITY;
-    v3 = (i3 < E) ? l[i3] : -INFINITY;
-    if (i0 >= E) i0 = 0x7FFFFFFF;
-    if (i1 >= E) i1 = 0x7FFFFFFF;
-    if (i2 >= E) i2 = 0x7FFFFFFF;
-    if (i3 >= E) i3 = 0x7FFFFFFF;
-    // sorting network for 4 keys
-    cswap(v0, i0, v1, i1);
-    cswap(v2, i2, v3, i3);
-    cswap(v0, i0, v2, i2);
-    cswap(v1, i1, v3, i3);
-    cswap(v1, i1, v2, i2);
-    float val[kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        if (s < K) {
-            const float m = wave_max_f32(v0);
-            const uint64_t hit = __ballot(v0 == m);
-            int gi;
-            if (__popcll(hit) == 1)  // usual case: one lane holds the maximum
-                gi = __builtin_amdgcn_readlane(i0, __ffsll((unsigned long long)hit) - 1);
-            else                     // equal logits: lowest expert index wins
-                gi = wave_min_i32(v0 == m ? i0 : 0x7FFFFFFF);
-            idx[s] = gi;
-            val[s] = m;
-            if (i0 == gi) {  // pop the head
-                v0 = v1; i0 = i1;
-                v1 = v2; i1 = i2;
-                v2 = v3; i2 = i3;
-                v3 = -INFINITY; i3 = 0x7FFFFFFF;
-            }
-        }
-    }
-    // softmax over the selected logits (val[0] is the largest)
-    float sum = 0.0f;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        if (s < K) {
-            w[s] = __expf(val[s] - val[0]);
-            sum += w[s];
-        }
-    }
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
-        if (s < K) w[s] *= inv;
-}
-
-// ---------------------------------------------------------------------------
 // router logits for large batches.  A block (4 waves) computes a 16-token x
 // 16-expert tile; wave w owns experts 4w..4w+3 of the tile.  Per 256-column
 // group the block stages the 16 token rows (8 KiB) in LDS once, instead of
@@ -327,7 +246,7 @@ hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const fl
     else
         router_small_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws.logits);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || T == 1) return e;  // a single token is routed by the gate/up kernel
     route_small_kernel<<<1, kRouteThreads, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
                                                     ws.counts, ws.offsets, ws.active, ws.perm,
                                                     ws.inv);
