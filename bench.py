@@ -334,6 +334,10 @@ def main():
         log("prefill T=2048")
         pre = b.run(W.PREFILL, 30, 5, 2048, replay=10)
         extra["prefill_t2048"] = prefill_report(pre, algorithmic(W.PREFILL, W.PREFILL.experts, 2048))
+        log("VQ13R8 decode T=1 (large-batch kernels)")
+        vqd = b.run(W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1"), 200, 20, 1,
+                    layers=b.vq_layers(), replay=100)
+        extra["vq_decode_t1"] = vqd
         log("VQ13R8 prefill T=2048")
         vq = b.run(W.VQ_PREFILL, 30, 5, 2048, layers=b.vq_layers(), replay=10)
         extra["vq_prefill_t2048"] = prefill_report(

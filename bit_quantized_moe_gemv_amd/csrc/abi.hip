@@ -209,8 +209,9 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
     }
     hipError_t err = hipSuccess;
     if (path == MOE_PATH_DECODE) {
-        err = staged(L, slot, MOE_STAGE_ROUTER, st,
-                         [&] { return launch_router_route_small(s, x, router_w, T, ws, st); });
+        err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
+            return launch_router_route_small(s, x, router_w, T, ws, st, false);
+        });
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_GATEUP, st,
                          [&] { return launch_decode_gateup(s, T, x, packed, ws, st); });
@@ -218,12 +219,19 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
             err = staged(L, slot, MOE_STAGE_DOWN, st,
                          [&] { return launch_decode_down(s, T, packed, ws, out, st); });
     } else {
-        err = staged(L, slot, MOE_STAGE_ROUTER, st,
-                     [&] { return launch_router(s, x, router_w, T, ws.logits, st); });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_PERMUTE, st, [&] { return launch_permute(s, T, ws, st); });
+        if (T <= kDecodeMaxTokens) {  // small batch (a VQ layer, or a forced path)
+            err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
+                return launch_router_route_small(s, x, router_w, T, ws, st, true);
+            });
+        } else {
+            err = staged(L, slot, MOE_STAGE_ROUTER, st,
+                         [&] { return launch_router(s, x, router_w, T, ws.logits, st); });
+            if (err == hipSuccess)
+                err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
+            if (err == hipSuccess)
+                err = staged(L, slot, MOE_STAGE_PERMUTE, st,
+                             [&] { return launch_permute(s, T, ws, st); });
+        }
         const bool vq = s.fmt == MOE_FMT_VQ13R8;
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_GATEUP, st, [&] {
@@ -289,8 +297,9 @@ int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void
         hipError_t e = hipSuccess;
         switch (stage) {
             case MOE_STAGE_ROUTER:
-                e = decode ? launch_router_route_small(s, x, router_w, T, ws, st)
-                           : launch_router(s, x, router_w, T, ws.logits, st);
+                e = decode                  ? launch_router_route_small(s, x, router_w, T, ws, st, false)
+                    : T <= kDecodeMaxTokens ? launch_router_route_small(s, x, router_w, T, ws, st, true)
+                                            : launch_router(s, x, router_w, T, ws.logits, st);
                 break;
             case MOE_STAGE_SELECT: e = launch_topk(s, T, ws, st); break;
             case MOE_STAGE_PERMUTE: e = launch_permute(s, T, ws, st); break;

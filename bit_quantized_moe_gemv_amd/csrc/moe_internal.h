@@ -56,8 +56,11 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws);
 // ---- launchers (each returns hipSuccess or the launch error) ----
 hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int T, float *logits,
                          hipStream_t st);
+// Small batches (T <= 16): logits, then the routing kernel -- except for a
+// single token when route_single is false (the batch-1 decode gate/up kernel
+// routes it).
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
-                                     const Workspace &ws, hipStream_t st);
+                                     const Workspace &ws, hipStream_t st, bool route_single);
 hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 bool decode_supported(const Shape &s);

@@ -239,14 +239,15 @@ static void router_small_launch(const Shape &s, dim3 grid, hipStream_t st, const
 }
 
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
-                                     const Workspace &ws, hipStream_t st) {
+                                     const Workspace &ws, hipStream_t st, bool route_single) {
     if (T < 1 || T > kDecodeMaxTokens || s.H / 256 > 32) return hipErrorInvalidValue;
     if (T == 1)
         router_small_launch<1>(s, dim3(1, (s.E + 3) / 4), st, x, wr, T, ws.logits);
     else
         router_small_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws.logits);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || T == 1) return e;  // a single token is routed by the gate/up kernel
+    // a single token is routed by the batch-1 gate/up kernel unless route_single
+    if (e != hipSuccess || (T == 1 && !route_single)) return e;
     route_small_kernel<<<1, kRouteThreads, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
                                                     ws.counts, ws.offsets, ws.active, ws.perm,
                                                     ws.inv);

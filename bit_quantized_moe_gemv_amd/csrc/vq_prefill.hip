@@ -32,12 +32,9 @@
 // (0..7) of the super-step uses its vector s, i.e. columns 64q+8s..+7.  The B
 // operand of lane (m, q) at K step s is therefore x[m][256J+64q+8s..+7];
 // sub-step u holds K steps 2u and 2u+1.
-#include "moe_internal.h"
+#include "vq_common.h"
 
 namespace bqmoe {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 constexpr int kVqWaves = 8;  // two per SIMD, sharing the books
 constexpr int kVqThreads = kVqWaves * 64;
@@ -52,18 +49,6 @@ struct VqLds {
     uint8_t b[kVqRing][2][4][64][16];  // [slot][K step parity][q][token][8 fp16]
 };
 
-__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-}
-
-// Exponent s with max * 2^-s in [2^14, 2^15), from the fp32 bits of a row's
-// largest magnitude (0 for an all-zero row).
-__device__ __forceinline__ int fp16_row_exponent(uint32_t maxbits) {
-    if (maxbits == 0) return 0;
-    const int e = (int)(maxbits >> 23);
-    return (e == 0 ? -126 : e - 127) - 14;
-}
-
 template <int N>
 __device__ __forceinline__ void vq_wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -73,14 +58,6 @@ __device__ __forceinline__ void vq_wait_vmcnt() {
 __device__ __forceinline__ void vq_stage_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: loads stay in flight
     __builtin_amdgcn_s_barrier();
-}
-
-// Block-wide maximum of non-negative fp32 bit patterns, compared as integers
-// (the same order as the magnitudes, subnormals included).
-__device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *slot) {
-    atomicMax(slot, v);
-    __syncthreads();
-    return *slot;
 }
 
 // ---------------------------------------------------------------------------
@@ -154,27 +131,15 @@ __global__ __launch_bounds__(256) void vq_hpack_kernel(const float *__restrict__
     if (threadIdx.x == 0) hexp[blockIdx.x] = s;
 }
 
-// 12-bit index s (0..7) of a lane's 96-bit code12 run (little-endian stream).
-template <int S>
-__device__ __forceinline__ uint32_t code12_at(const uint32_t (&c)[6]) {
-    constexpr int b = 12 * S, k = b / 32, sh = b % 32;
-    if (sh + 12 <= 32 || k == 2) return (c[k] >> sh) & 0xFFFu;
-    return __builtin_amdgcn_alignbit(c[k + 1], c[k], sh) & 0xFFFu;
-}
-
 // A operand of K step S for one row group: Cb[i13] + Rb[i8] in fp16.
 // c[0..2] code12, c[3..4] res, c[5] plane byte.
 template <int S>
 __device__ __forceinline__ void gather_a(const uint32_t (&c)[6], const VqLds &lds, uint4 &cbv,
                                          uint4 &rbv) {
-    const uint32_t i13 = code12_at<S>(c) | (((c[5] >> S) & 1u) << 12);
-    const uint32_t i8 = (c[3 + S / 4] >> (8 * (S % 4))) & 0xFFu;
+    uint32_t i13, i8;
+    vq_indices<S>(c, i13, i8);
     cbv = lds.cb[i13];
     rbv = lds.rb[i8];
-}
-
-__device__ __forceinline__ f16x8 add_f16x8(uint4 a, uint4 b) {
-    return __builtin_bit_cast(f16x8, a) + __builtin_bit_cast(f16x8, b);
 }
 
 // One sub-step (two K steps) of a wave: 2 x 4 groups x 4 token tiles MFMAs.
@@ -413,12 +378,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
 // Persistent grid: one block per CU (the books fill most of the LDS), a
 // multiple of 8 when there is enough work so every XCD gets the same share.
 static int vq_grid(int items) {
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu < 1)
-        ncu = 256;
-    int g = min(items, ncu);
+    int g = min(items, device_cu_count());
     if (g >= 8) g &= ~7;
     return max(g, 1);
 }
