@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbqmoe.so")
-SOURCES = ["abi.hip", "route.hip", "decode.hip", "prefill.hip", "vq_prefill.hip"]
+SOURCES = ["abi.hip", "route.hip", "decode.hip", "prefill.hip", "vq_prefill.hip", "vq_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -192,9 +192,9 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
         return MOE_EINVAL;
     int path = L->desc.force_path;
     if (path == MOE_PATH_AUTO)
-        path = (T <= kDecodeMaxTokens && decode_supported(L->shape)) ? MOE_PATH_DECODE
-                                                                     : MOE_PATH_PREFILL;
-    if (path == MOE_PATH_DECODE && T > kDecodeMaxTokens) return MOE_EINVAL;
+        path = (T <= decode_max_tokens(L->shape) && decode_supported(L->shape)) ? MOE_PATH_DECODE
+                                                                             : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_DECODE && T > decode_max_tokens(L->shape)) return MOE_EINVAL;
     const Shape &s = L->shape;
     const Workspace &ws = L->ws;
     hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -93,47 +93,16 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
             int sel[kMaxTopK];
             float wt[kMaxTopK];
             wave_topk(logits, E, K, sel, wt);
-            const int ln = threadIdx.x;
-            // ascending rank of each selected expert = its route position
             int pos[kMaxTopK];
-#pragma unroll
-            for (int s2 = 0; s2 < kMaxTopK; ++s2) {
-                pos[s2] = 0;
-#pragma unroll
-                for (int j = 0; j < kMaxTopK; ++j)
-                    if (s2 < K && j < K) pos[s2] += sel[j] < sel[s2];
-            }
+            single_token_positions(sel, K, pos);
             int mine = sel[0];
 #pragma unroll
             for (int s2 = 0; s2 < kMaxTopK; ++s2)
                 if (s2 < K && pos[s2] == slot) mine = sel[s2];
-            if (ln == 0) s_e = mine;
-            if (blockIdx.x == 0 && blockIdx.y == 0) {
-#pragma unroll
-                for (int s2 = 0; s2 < kMaxTopK; ++s2)
-                    if (s2 < K && ln == s2) {
-                        idx_out[s2] = sel[s2];
-                        w_out[s2] = wt[s2];
-                        perm[pos[s2]] = s2;
-                        inv[s2] = pos[s2];
-                        active[1 + pos[s2]] = sel[s2];
-                    }
-                if (ln == 0) {
-                    active[0] = K;
-                    offsets[E] = K;
-                }
-                for (int ee = ln; ee < E; ee += 64) {
-                    int c = 0, below = 0;
-#pragma unroll
-                    for (int j = 0; j < kMaxTopK; ++j)
-                        if (j < K) {
-                            c += sel[j] == ee;
-                            below += sel[j] < ee;
-                        }
-                    counts[ee] = c;
-                    offsets[ee] = below;
-                }
-            }
+            if (threadIdx.x == 0) s_e = mine;
+            if (blockIdx.x == 0 && blockIdx.y == 0)
+                publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active, counts,
+                                     offsets);
         }
         lds_barrier();
         e = s_e;
@@ -389,14 +358,18 @@ static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
 }
 
 bool decode_supported(const Shape &s) {
+    if (s.fmt == MOE_FMT_VQ13R8) return vq_decode_supported(s);
     const int nj = s.H / 256;
     const bool h_ok = nj == 1 || nj == 2 || nj == 4 || nj == 8 || nj == 16 || nj == 32;
     const bool i_ok = s.I == 128 || s.I == 256 || s.I == 512 || s.I == 1024 || s.I == 2048;
     return s.fmt == MOE_FMT_MXFP4 && h_ok && i_ok;
 }
 
+int decode_max_tokens(const Shape &s) { return s.fmt == MOE_FMT_VQ13R8 ? 1 : kDecodeMaxTokens; }
+
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
+    if (s.fmt == MOE_FMT_VQ13R8) return launch_vq_decode_gateup(s, T, x, packed, ws, st);
     switch (s.H / 256) {
         case 1: return gateup_launch_tc<1>(s, T, x, packed, ws, st);
         case 2: return gateup_launch_tc<2>(s, T, x, packed, ws, st);
@@ -419,6 +392,7 @@ static hipError_t down_launch(const Shape &s, int T, const uint8_t *packed, cons
 
 hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                               float *out, hipStream_t st) {
+    if (s.fmt == MOE_FMT_VQ13R8) return launch_vq_decode_down(s, T, packed, ws, out, st);
     if (s.I > kDnMaxI || T * s.K > kDnMaxR) return hipErrorInvalidValue;
     switch (s.I) {
         case 128:

@@ -64,6 +64,12 @@ hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const fl
 hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_t st);
 bool decode_supported(const Shape &s);
+int decode_max_tokens(const Shape &s);  // largest T the decode kernels take
+bool vq_decode_supported(const Shape &s);
+hipError_t launch_vq_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
+                                   const Workspace &ws, hipStream_t st);
+hipError_t launch_vq_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
+                                 float *out, hipStream_t st);
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st);
 hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
@@ -191,14 +197,21 @@ __device__ __forceinline__ void cswap(float &va, int &ia, float &vb, int &ib) {
     ia = ti;
 }
 
-__device__ inline void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
+// The lane's four logits (experts lane + 64j), -inf past E.  Issued as
+// unconditional loads (clamped index) so a caller can count them.
+__device__ __forceinline__ void topk_load(const float *__restrict__ l, int E, float (&v)[4]) {
     const int lane = threadIdx.x & 63;
-    float v0, v1, v2, v3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = l[min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (lane + 64 * j >= E) v[j] = -INFINITY;
+}
+
+__device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, int *idx, float *w) {
+    const int lane = threadIdx.x & 63;
+    float v0 = lv[0], v1 = lv[1], v2 = lv[2], v3 = lv[3];
     int i0 = lane, i1 = lane + 64, i2 = lane + 128, i3 = lane + 192;
-    v0 = (i0 < E) ? l[i0] : -INFINITY;
-    v1 = (i1 < E) ? l[i1] : -INFINITY;
-    v2 = (i2 < E) ? l[i2] : -INFINITY;
-    v3 = (i3 < E) ? l[i3] : -INFINITY;
     if (i0 >= E) i0 = 0x7FFFFFFF;
     if (i1 >= E) i1 = 0x7FFFFFFF;
     if (i2 >= E) i2 = 0x7FFFFFFF;
@@ -243,6 +256,60 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int K, int 
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s)
         if (s < K) w[s] *= inv;
+}
+
+__device__ inline void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
+    float v[4];
+    topk_load(l, E, v);
+    wave_topk_vals(v, E, K, idx, w);
+}
+
+// Route positions of a single token: slot s goes to position pos[s], the rank
+// of its expert among the selected ones (ascending), which is the order the
+// counting sort gives.
+__device__ __forceinline__ void single_token_positions(const int *sel, int K, int *pos) {
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        pos[s] = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (s < K && j < K) pos[s] += sel[j] < sel[s];
+    }
+}
+
+// Writes a single token's routing, computed identically by every lane of one
+// wave, in the layout the routing kernels produce: idx/w in slot order,
+// perm/inv between route ids and positions, the active expert list, and
+// counts/offsets over all E experts.
+__device__ inline void publish_single_token(const int *sel, const float *wt, const int *pos, int E,
+                                            int K, int32_t *idx_out, float *w_out, int32_t *perm,
+                                            int32_t *inv, int32_t *active, int32_t *counts,
+                                            int32_t *offsets) {
+    const int ln = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+        if (s < K && ln == s) {
+            idx_out[s] = sel[s];
+            w_out[s] = wt[s];
+            perm[pos[s]] = s;
+            inv[s] = pos[s];
+            active[1 + pos[s]] = sel[s];
+        }
+    if (ln == 0) {
+        active[0] = K;
+        offsets[E] = K;
+    }
+    for (int ee = ln; ee < E; ee += 64) {
+        int c = 0, below = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < K) {
+                c += sel[j] == ee;
+                below += sel[j] < ee;
+            }
+        counts[ee] = c;
+        offsets[ee] = below;
+    }
 }
 
 }  // namespace bqmoe

@@ -71,19 +71,21 @@ enum {
 enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2 };
 
 /* Path selection: AUTO uses the weight-streaming decode kernels for batches of
- * at most MOE_DECODE_MAX_TOKENS tokens and the grouped-GEMM prefill kernels
- * above that; DECODE and PREFILL force one of them (DECODE requires
- * T <= MOE_DECODE_MAX_TOKENS).  The decode kernels exist for MXFP4 layers
- * with hidden/256 and inter powers of two (inter <= 2048): other layers,
- * VQ13R8 ones included, run the grouped-GEMM kernels at every batch size, and
- * forcing DECODE on them returns MOE_EUNSUPPORTED.
+ * at most MOE_DECODE_MAX_TOKENS tokens (MXFP4) or of one token (VQ13R8) and
+ * the grouped-GEMM prefill kernels above that; DECODE and PREFILL force one of
+ * them (DECODE with a larger T returns MOE_EINVAL).  The decode kernels exist
+ * for MXFP4 layers with hidden/256 and inter powers of two (inter <= 2048) and
+ * for VQ13R8 layers with hidden/256 a power of two up to 16 and inter one of
+ * 256, 512, 1024, 2048: other layers run the grouped-GEMM kernels at every
+ * batch size, and forcing DECODE on them returns MOE_EUNSUPPORTED.
  *
  * Numerics of the grouped-GEMM kernels: MXFP4 weights are exact in bf16 and
  * the intermediate h enters the down projection as an exact bf16 pair
  * (hi + lo); VQ13R8 weights enter as fp16(Cb + Rb) (one rounding, relative
  * error <= 2^-11) with the row gain applied in fp32, and x and h as fp16 rows
- * scaled by an exact power of two per row (relative error <= 2^-11 for h).
- * All products accumulate in fp32. */
+ * scaled by an exact power of two per row (relative error <= 2^-11 for h);
+ * the VQ13R8 decode kernels use the same operands.  All products accumulate
+ * in fp32. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 #define MOE_DECODE_MAX_TOKENS 16
 

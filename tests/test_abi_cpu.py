@@ -117,8 +117,8 @@ def test_forced_decode_rejects_large_batches(lib):
 
 def test_vq_descriptor_sizes_and_paths(lib):
     """VQ13R8 layers: packed size = books + experts; intermediate widths must be
-    multiples of 256; the batch-1 decode kernels are MXFP4-only, so forcing
-    the decode path on a VQ layer is reported as unsupported."""
+    multiples of 256; forcing the decode path on a shape the batch-1 VQ
+    kernels do not cover is reported as unsupported."""
     import workloads as W
     for h, i, e in ((256, 256, 8), (4096, 2048, 256)):
         assert bq.packed_size(h, i, e, 2, fmt=bq.MOE_FMT_VQ13R8) == \
@@ -126,9 +126,14 @@ def test_vq_descriptor_sizes_and_paths(lib):
     with pytest.raises(bq.MoeError) as ei:
         bq.packed_size(256, 128, 8, 2, fmt=bq.MOE_FMT_VQ13R8)
     assert ei.value.status == bq.MOE_EINVAL
-    with pytest.raises(bq.MoeError) as ei:
-        bq.workspace_size(256, 256, 8, 2, 16, bq.MOE_FMT_VQ13R8, bq.MOE_PATH_DECODE)
-    assert ei.value.status == bq.MOE_EUNSUPPORTED
+    # batch-1 decode kernels exist for hidden/256 in {1, 2, 4, 8, 16} and
+    # inter in {256, 512, 1024, 2048}; other shapes cannot be forced to decode
+    for h, i in ((256, 256), (512, 2048), (4096, 2048), (4096, 256)):
+        bq.workspace_size(h, i, 8, 2, 16, bq.MOE_FMT_VQ13R8, bq.MOE_PATH_DECODE)
+    for h, i in ((768, 512), (8192, 2048), (4096, 4096), (1024, 768)):
+        with pytest.raises(bq.MoeError) as ei:
+            bq.workspace_size(h, i, 8, 2, 16, bq.MOE_FMT_VQ13R8, bq.MOE_PATH_DECODE)
+        assert ei.value.status == bq.MOE_EUNSUPPORTED
     # the VQ workspace adds the fp16 copies of x and h and their row exponents
     mx = bq.workspace_size(4096, 2048, 256, 8, 2048, bq.MOE_FMT_MXFP4)
     vq = bq.workspace_size(4096, 2048, 256, 8, 2048, bq.MOE_FMT_VQ13R8)
