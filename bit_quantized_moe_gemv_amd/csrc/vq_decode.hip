@@ -7,22 +7,23 @@
 // fp16) are copied into LDS by every block at its start (from L2 after the
 // first block), so a gather is two 16-byte LDS reads.
 //
-// The dot products run on the matrix core with the gathered vectors as the A
-// operand (16 weight rows x 32 K, lane (n, q): row n, vectors 8q..8q+7 of a
-// 256-column tile, exactly a lane's contiguous run of index bytes) and the
-// activation as B, the same in all 16 columns: lanes (n, q) all read the one
-// 16-byte piece of x or h that K step s needs, an LDS broadcast, and column 0
-// of the result is the dot product.  As in the large-batch kernels the A
-// operand is Cb + Rb rounded once to fp16 and the activations enter as fp16
-// rows scaled by an exact power of two.
+// Lane (n, q) of a wave owns, in each 16-row x 256-column tile, row n's
+// vectors 8q..8q+7 -- exactly its contiguous run of index bytes.  At K step s
+// it gathers Cb[i13] and Rb[i8] of vector 8q+s and takes both dot products
+// with the matching 16-byte piece of the activation (lanes of one q read the
+// same piece: an LDS broadcast) on the vector ALU (v_dot2_f32_f16: fp16 pairs,
+// exact products, fp32 sums); the four lanes of a row add up at the end.  The
+// books' values enter unrounded; the activations enter as fp16 rows scaled by
+// an exact power of two, as in the large-batch kernels.  (At one token the
+// matrix core would waste 15 of its 16 columns.)
 //
 // Kernels (one token, k routes):
 //  * vq_dec_gateup: block = 4 (gate, up) row-group pairs of one route (8
 //    groups of 16 rows).  Each wave streams GW groups over TJ tiles of K; the
 //    partial dot products meet in LDS and the block applies the row gains,
 //    2^s_x and SwiGLU, writing h (fp32, route-position order).  Every block
-//    selects the top-k from the router logits itself; block 0 publishes the
-//    routing.
+//    selects the top-k from the router logits itself (one wave); block 0
+//    publishes the routing.
 //  * vq_dec_down: block = one output row group (16 rows) for all k routes.
 //    Each wave streams one route's tiles over a quarter of K; the routes go
 //    through in two phases of four, h of the phase's routes staged in LDS as
@@ -49,39 +50,45 @@ struct VdGuLds {
     uint4 x16[kVdMaxH / 8];   // fp16 x * 2^-s, piece (J, s, q) at (8J + s)*4 + q
     float red[kVdWaves][kVdGroups][16];  // [K slice][group][row]
     float wmax[kVdWaves];
+    int expert;
 };
 
 struct VdDnLds {
     VdBooks bk;
     uint4 h16[4][kVdMaxI / 8];  // one phase's 4 routes, fp16 h * 2^-s, same piece order
     float red[kVdWaves][16];    // [wave][row]
-    float wmax[kVdWaves][4];
+    uint32_t rmax[8];           // per route: largest |h| (fp32 bits)
 };
 
-// The books reach LDS through registers: a thread loads kBookLoads 16-byte
-// pieces (the last repeats for threads past the end, rewriting the same bytes)
-// early, and stores them once its own routing-dependent loads are issued.
-// (An LDS-direct copy would leave the compiler unable to count the vector
-// loads behind it, so every later wait would be for all loads in flight.)
+// The books reach LDS through registers: each of NT threads loads kBookLoads
+// 16-byte pieces (the last repeats for threads past the end, rewriting the
+// same bytes).  (An LDS-direct copy would leave the compiler unable to count
+// the vector loads behind it, so every later wait would be for all loads in
+// flight.)
 constexpr int kBookPieces = kVqEntries + kVqResEntries;  // 16-byte pieces
-constexpr int kBookLoads = (kBookPieces + kVdThreads - 1) / kVdThreads;
+constexpr int kBookLoads = (kBookPieces + kVdThreads - 65) / (kVdThreads - 64);  // 15 waves
 
-__device__ __forceinline__ void load_books(const uint8_t *packed, int tid, uint4 (&bv)[kBookLoads]) {
+template <int NT>
+__device__ __forceinline__ void load_books(const uint8_t *packed, int t, uint4 (&bv)[kBookLoads]) {
+    static_assert(NT * kBookLoads >= kBookPieces, "book split");
     const uint4 *src = reinterpret_cast<const uint4 *>(packed);
 #pragma unroll
-    for (int j = 0; j < kBookLoads; ++j) bv[j] = src[min(tid + kVdThreads * j, kBookPieces - 1)];
+    for (int j = 0; j < kBookLoads; ++j) bv[j] = src[min(t + NT * j, kBookPieces - 1)];
 }
 
-__device__ __forceinline__ void store_books(VdBooks &bk, int tid, const uint4 (&bv)[kBookLoads]) {
+template <int NT>
+__device__ __forceinline__ void store_books(VdBooks &bk, int t, const uint4 (&bv)[kBookLoads]) {
     uint4 *dst = reinterpret_cast<uint4 *>(&bk);
 #pragma unroll
-    for (int j = 0; j < kBookLoads; ++j) dst[min(tid + kVdThreads * j, kBookPieces - 1)] = bv[j];
+    for (int j = 0; j < kBookLoads; ++j) dst[min(t + NT * j, kBookPieces - 1)] = bv[j];
 }
 
-// One K step (vector S of the lane's runs) for G groups against B piece b.
+// One K step (vector S of the lane's runs) for G groups against the
+// activation piece b: two fp32 dot products per group, Cb[i13] . b and
+// Rb[i8] . b, each over the eight fp16 pairs with exact products.
 template <int S, int G>
 __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBooks &bk, uint4 b,
-                                         f32x4 (&acc)[G]) {
+                                         float (&acc)[G][2]) {
     uint4 cbv[G], rbv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -90,16 +97,29 @@ __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBoo
         cbv[g] = bk.cb[i13];
         rbv[g] = bk.rb[i8];
     }
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(add_f16x8(cbv[g], rbv[g]),
-                                                        __builtin_bit_cast(f16x8, b), acc[g], 0,
-                                                        0, 0);
+    for (int g = 0; g < G; ++g) {
+        const uint32_t cw[4] = {cbv[g].x, cbv[g].y, cbv[g].z, cbv[g].w};
+        const uint32_t rw[4] = {rbv[g].x, rbv[g].y, rbv[g].z, rbv[g].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc[g][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, cw[w]),
+                                               __builtin_bit_cast(f16x2, bw[w]), acc[g][0], false);
+            acc[g][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, rw[w]),
+                                               __builtin_bit_cast(f16x2, bw[w]), acc[g][1], false);
+        }
+    }
+    // The sums leave every step through an empty asm: left free, the compiler
+    // defers all the dot products to the end of the tile and keeps every
+    // gathered vector alive until then.
+#pragma unroll
+    for (int g = 0; g < G; ++g) asm volatile("" : "+v"(acc[g][0]), "+v"(acc[g][1]));
 }
 
 template <int G>
 __device__ __forceinline__ void vd_tile(const uint32_t (&cr)[G][6], const VdBooks &bk,
-                                        const uint4 *bpieces, int q, f32x4 (&acc)[G]) {
+                                        const uint4 *bpieces, int q, float (&acc)[G][2]) {
     vd_kstep<0, G>(cr, bk, bpieces[0 * 4 + q], acc);
     vd_kstep<1, G>(cr, bk, bpieces[1 * 4 + q], acc);
     vd_kstep<2, G>(cr, bk, bpieces[2 * 4 + q], acc);
@@ -108,6 +128,15 @@ __device__ __forceinline__ void vd_tile(const uint32_t (&cr)[G][6], const VdBook
     vd_kstep<5, G>(cr, bk, bpieces[5 * 4 + q], acc);
     vd_kstep<6, G>(cr, bk, bpieces[6 * 4 + q], acc);
     vd_kstep<7, G>(cr, bk, bpieces[7 * 4 + q], acc);
+}
+
+// A row's dot product from its four lanes (n, q = 0..3): every lane of row n
+// gets the sum.
+__device__ __forceinline__ float row_sum(const float (&a)[2]) {
+    float v = a[0] + a[1];
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
 }
 
 // Index into the (J, s, q) piece order of the column c (a multiple of 4) of a
@@ -139,30 +168,47 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     const int wa = min(wave, NWA - 1);
     const int gset = wa / NSL, js = wa % NSL;  // groups [gset*GW, +GW), tiles [js*TJ, +TJ)
 
-    float lv[4];
-    topk_load(logits, E, lv);
-    const int nx = H / 8;
-    const uint4 xv = reinterpret_cast<const uint4 *>(x)[min(tid, nx - 1)];
-
-    int sel[kMaxTopK], pos[kMaxTopK];
-    float wt[kMaxTopK];
-    wave_topk_vals(lv, E, K, sel, wt);
-    single_token_positions(sel, K, pos);
-
+    // Wave 0 selects the routes while the other waves copy the books, which
+    // do not depend on the routing, into LDS.
     const int ipg = I / 16;                       // gate row groups
     const int p = (kVdPairs * blockIdx.x) / ipg;  // route position of this block
     const int i0 = (kVdPairs * blockIdx.x) % ipg;
-    int e = sel[0];
+    const int nx = H / 8;
+    const uint4 xv = reinterpret_cast<const uint4 *>(x)[min(tid, nx - 1)];
+    if (wave == 0) {
+        float lv[4];
+        topk_load(logits, E, lv);
+        int sel[kMaxTopK], pos[kMaxTopK];
+        float wt[kMaxTopK];
+        wave_topk_vals(lv, E, K, sel, wt);
+        single_token_positions(sel, K, pos);
+        int e0 = sel[0];
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
-        if (s < K && pos[s] == p) e = sel[s];
-    e = __builtin_amdgcn_readfirstlane(e);
+        for (int s = 0; s < kMaxTopK; ++s)
+            if (s < K && pos[s] == p) e0 = sel[s];
+        if (lane == 0) lds.expert = e0;
+        if (blockIdx.x == 0)
+            publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active, counts,
+                                 offsets);
+    } else {
+        uint4 bv[kBookLoads];
+        load_books<kVdThreads - 64>(packed, tid - 64, bv);
+        store_books<kVdThreads - 64>(lds.bk, tid - 64, bv);
+    }
+    uint32_t mb = 0;  // largest |x| bits of the thread's 8 values
+    {
+        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mb = max(mb, (w4[k] & 0x7FFFu) << 16);
+            mb = max(mb, w4[k] & 0x7FFF0000u);
+        }
+    }
+    const float wm = wave_max_f32(__uint_as_float(mb));
+    if (lane == 0) lds.wmax[wave] = wm;
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(lds.expert);
 
-    // the books (L2-resident after the first blocks) go out first, then the
-    // weight indices; compute starts once both are in
-    uint4 bv[kBookLoads];
-    load_books(packed, tid, bv);
-    __builtin_amdgcn_sched_barrier(0);
     const VqMatrix m(packed + kVqBooksBytes + (size_t)e * expert_bytes, (size_t)2 * I, (size_t)H);
     uint32_t cr[TJ][GW][6];
 #pragma unroll
@@ -177,21 +223,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     const int grow = 16 * (i0 + ((tid >> 4) & (kVdPairs - 1))) + (tid & 15);
     const uint32_t gg = m.gain[grow], gu = m.gain[I + grow];
 
-    store_books(lds.bk, tid, bv);
-
     // x -> fp16 * 2^-s_x, s_x from the row's largest magnitude
-    uint32_t mb = 0;
-    {
-        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            mb = max(mb, (w4[k] & 0x7FFFu) << 16);
-            mb = max(mb, w4[k] & 0x7FFF0000u);
-        }
-    }
-    const float wm = wave_max_f32(__uint_as_float(mb));
-    if (lane == 0) lds.wmax[wave] = wm;
-    __syncthreads();
     float xm = lds.wmax[0];
 #pragma unroll
     for (int w2 = 1; w2 < kVdWaves; ++w2) xm = fmaxf(xm, lds.wmax[w2]);
@@ -211,17 +243,16 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     }
     __syncthreads();
 
-    f32x4 acc[GW];
+    float acc[GW][2];
 #pragma unroll
-    for (int g = 0; g < GW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < GW; ++g) acc[g][0] = acc[g][1] = 0.f;
 #pragma unroll
     for (int u = 0; u < TJ; ++u) vd_tile<GW>(cr[u], lds.bk, &lds.x16[32 * (js * TJ + u)], q, acc);
 
-    if (n == 0 && wave < NWA) {
 #pragma unroll
-        for (int g = 0; g < GW; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lds.red[js][gset * GW + g][4 * q + j] = acc[g][j];
+    for (int g = 0; g < GW; ++g) {
+        const float v = row_sum(acc[g]);
+        if (q == 0 && wave < NWA) lds.red[js][gset * GW + g][n] = v;
     }
     __syncthreads();
     if (tid < 16 * kVdPairs) {
@@ -236,8 +267,6 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         const float uv = ldexpf(us * f16_bits_to_f32(gu), xs);
         h[(size_t)p * I + grow] = silu_f32(gv) * uv;
     }
-    if (blockIdx.x == 0 && wave == 0)  // after the weight stream, so its stores do not delay it
-        publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active, counts, offsets);
 }
 
 // ---------------------------------------------------------------------------
@@ -262,8 +291,9 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     const bool jlive = jq * TJ < NJD;
     const int j0 = min(jq * TJ, NJD - TJ);  // clamped for loads
 
+    if (tid < 8) lds.rmax[tid] = 0;
     uint4 bv[kBookLoads];
-    load_books(packed, tid, bv);
+    load_books<kVdThreads>(packed, tid, bv);
     int ex[2];
     float wgt[2];
 #pragma unroll
@@ -283,45 +313,33 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
 
     const size_t dn_off = vq_down_offset((size_t)H, (size_t)I);
     uint32_t cr[2][TJ][1][6];
-    uint2 gn[2];  // gains of rows 16rg + 4q .. +3
+    uint32_t gn[2];  // gain of row 16rg + n
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const VqMatrix m(packed + kVqBooksBytes + (size_t)ex[f] * expert_bytes + dn_off,
                          (size_t)H, (size_t)I);
 #pragma unroll
         for (int u = 0; u < TJ; ++u) m.load((size_t)rg * NJD + j0 + u, lane, cr[f][u][0]);
-        gn[f] = *reinterpret_cast<const uint2 *>(m.gain + 16 * rg + 4 * q);
+        gn[f] = m.gain[16 * rg + n];
     }
 
-    store_books(lds.bk, tid, bv);
-    // per-route exponents: wave maxima of the four routes it holds
+    store_books<kVdThreads>(lds.bk, tid, bv);
+    __syncthreads();
+    // per-route exponents from the largest |h| (non-negative floats order as
+    // their bit patterns)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float a = fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)),
                               fmaxf(fabsf(hv[k].z), fabsf(hv[k].w)));
         const float mx = wave_max_f32(a);
-        if (lane == 0) lds.wmax[wave][k] = mx;
+        if (lane == 0) atomicMax(&lds.rmax[4 * hh + k], __float_as_uint(mx));
     }
     __syncthreads();
     int hs[2][4];
-    {
-        float rm[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) rm[r] = 0.f;
-        for (int w2 = 0; w2 < kVdWaves; ++w2) {
-            const int h2 = ((w2 * 64) / ncg) & 1;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float v = lds.wmax[w2][k];
-                rm[k] = h2 == 0 ? fmaxf(rm[k], v) : rm[k];
-                rm[4 + k] = h2 == 1 ? fmaxf(rm[4 + k], v) : rm[4 + k];
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) hs[r >> 2][r & 3] = fp16_row_exponent(__float_as_uint(rm[r]));
-    }
+    for (int r = 0; r < 8; ++r) hs[r >> 2][r & 3] = fp16_row_exponent(lds.rmax[r]);
 
-    f32x4 acc[2];
+    float acc[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         if (f > 0) __syncthreads();  // phase 0's readers are done with h16
@@ -340,23 +358,17 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
             }
         }
         __syncthreads();
-        f32x4 a1[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+        float a1[1][2] = {{0.f, 0.f}};
 #pragma unroll
         for (int u = 0; u < TJ; ++u) vd_tile<1>(cr[f][u], lds.bk, &lds.h16[r4][32 * (j0 + u)], q, a1);
-        acc[f] = a1[0];
+        acc[f] = row_sum(a1[0]);
     }
 
-    if (n == 0) {
+    if (q == 0) {
         const bool l0 = jlive && r4 < K, l1 = jlive && 4 + r4 < K;
-        const float s0 = ldexpf(wgt[0], hs[0][r4]), s1 = ldexpf(wgt[1], hs[1][r4]);
-        const uint32_t g0[4] = {gn[0].x & 0xFFFFu, gn[0].x >> 16, gn[0].y & 0xFFFFu, gn[0].y >> 16};
-        const uint32_t g1[4] = {gn[1].x & 0xFFFFu, gn[1].x >> 16, gn[1].y & 0xFFFFu, gn[1].y >> 16};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float c0 = l0 ? acc[0][j] * f16_bits_to_f32(g0[j]) * s0 : 0.f;
-            const float c1 = l1 ? acc[1][j] * f16_bits_to_f32(g1[j]) * s1 : 0.f;
-            lds.red[wave][4 * q + j] = c0 + c1;
-        }
+        const float c0 = l0 ? acc[0] * f16_bits_to_f32(gn[0]) * ldexpf(wgt[0], hs[0][r4]) : 0.f;
+        const float c1 = l1 ? acc[1] * f16_bits_to_f32(gn[1]) * ldexpf(wgt[1], hs[1][r4]) : 0.f;
+        lds.red[wave][n] = c0 + c1;
     }
     __syncthreads();
     if (tid < 16) {
