@@ -334,10 +334,14 @@ def main():
         log("prefill T=2048")
         pre = b.run(W.PREFILL, 30, 5, 2048, replay=10)
         extra["prefill_t2048"] = prefill_report(pre, algorithmic(W.PREFILL, W.PREFILL.experts, 2048))
-        log("VQ13R8 decode T=1 (large-batch kernels)")
+        log("VQ13R8 decode T=1")
         vqd = b.run(W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1"), 200, 20, 1,
                     layers=b.vq_layers(), replay=100)
         extra["vq_decode_t1"] = vqd
+        log("VQ13R8 verify T=16 (skewed routing)")
+        vqv = b.run(W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed"), 100, 10,
+                    16, layers=b.vq_layers(), replay=20)
+        extra["vq_verify_t16"] = vqv
         log("VQ13R8 prefill T=2048")
         vq = b.run(W.VQ_PREFILL, 30, 5, 2048, layers=b.vq_layers(), replay=10)
         extra["vq_prefill_t2048"] = prefill_report(

@@ -28,6 +28,8 @@ MOE_FMT_VQ13R8 = 2
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL = 2
+MOE_ROUTE_SOFTMAX = 0
+MOE_ROUTE_SIGMOID = 1
 MOE_DECODE_MAX_TOKENS = 16
 
 STAGES = ("router", "select", "permute", "gateup", "down", "combine")
@@ -62,6 +64,7 @@ class moe_layer_desc(ctypes.Structure):
         ("max_tokens", ctypes.c_int32),
         ("format", ctypes.c_int32),
         ("force_path", ctypes.c_int32),
+        ("routing", ctypes.c_int32),
     ]
 
 
@@ -111,15 +114,16 @@ def status_str(status: int) -> str:
     return load_library().moe_status_str(status).decode()
 
 
-def _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path) -> moe_layer_desc:
-    return moe_layer_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+def _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path,
+          routing=MOE_ROUTE_SOFTMAX) -> moe_layer_desc:
+    return moe_layer_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path, routing)
 
 
 def packed_size(hidden, inter, n_experts, top_k, max_tokens=1, fmt=MOE_FMT_MXFP4,
-                force_path=MOE_PATH_AUTO) -> int:
+                force_path=MOE_PATH_AUTO, routing=MOE_ROUTE_SOFTMAX) -> int:
     b = ctypes.c_size_t(0)
     rc = load_library().moe_packed_size(
-        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)),
+        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path, routing)),
         ctypes.byref(b))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_packed_size")
@@ -127,10 +131,10 @@ def packed_size(hidden, inter, n_experts, top_k, max_tokens=1, fmt=MOE_FMT_MXFP4
 
 
 def workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt=MOE_FMT_MXFP4,
-                   force_path=MOE_PATH_AUTO) -> int:
+                   force_path=MOE_PATH_AUTO, routing=MOE_ROUTE_SOFTMAX) -> int:
     b = ctypes.c_size_t(0)
     rc = load_library().moe_workspace_size(
-        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)),
+        ctypes.byref(_desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path, routing)),
         ctypes.byref(b))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_workspace_size")
@@ -160,14 +164,16 @@ class MoeLayer:
     packed format; the result is a [T, hidden] float32 tensor."""
 
     def __init__(self, hidden, inter, n_experts, top_k, max_tokens, fmt=MOE_FMT_MXFP4,
-                 force_path=MOE_PATH_AUTO, device="cuda"):
+                 force_path=MOE_PATH_AUTO, device="cuda", routing=MOE_ROUTE_SOFTMAX):
         import torch
 
         self._lib = load_library()
-        self.desc = _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+        self.desc = _desc(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path, routing)
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.max_tokens, self.fmt, self.force_path = max_tokens, fmt, force_path
-        ws_bytes = workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path)
+        self.routing_mode = routing
+        ws_bytes = workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt, force_path,
+                                  routing)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         h = ctypes.c_void_p(0)
         rc = self._lib.moe_layer_create(ctypes.byref(self.desc), _ptr(self.workspace), ws_bytes,

@@ -110,6 +110,7 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
     if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_EINVAL;
     if (d->max_tokens < 1 || d->max_tokens > 65536) return MOE_EINVAL;
     if (d->force_path < MOE_PATH_AUTO || d->force_path > MOE_PATH_PREFILL) return MOE_EINVAL;
+    if (d->routing != MOE_ROUTE_SOFTMAX && d->routing != MOE_ROUTE_SIGMOID) return MOE_EINVAL;
     if (d->format == MOE_FMT_MXFP4) {
         if (d->inter % 128) return MOE_EINVAL;
     } else if (d->format == MOE_FMT_VQ13R8) {
@@ -123,6 +124,7 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
         s->E = d->n_experts;
         s->K = d->top_k;
         s->fmt = d->format;
+        s->routing = d->routing;
         const size_t H = (size_t)d->hidden, I = (size_t)d->inter;
         if (d->format == MOE_FMT_MXFP4) {
             s->expert_bytes = 3 * I * H * 17 / 32;

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     int H, int I, int E, int K, int32_t *__restrict__ active, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, float *__restrict__ h, const float *__restrict__ logits,
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
-    int32_t *__restrict__ inv) {
+    int32_t *__restrict__ inv, bool sigmoid) {
     extern __shared__ __align__(16) uint16_t xs[];  // [TC][H]
     __shared__ float red[4][TC][16];
     const int slot = blockIdx.x;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
         if (threadIdx.x < 64) {
             int sel[kMaxTopK];
             float wt[kMaxTopK];
-            wave_topk(logits, E, K, sel, wt);
+            wave_topk(logits, E, K, sigmoid, sel, wt);
             int pos[kMaxTopK];
             single_token_positions(sel, K, pos);
             int mine = sel[0];
@@ -346,7 +346,8 @@ static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const 
     dim3 grid(slots, s.I / 16);
     decode_gateup_mxfp4<NJ, TC, R1><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.active, ws.offsets, ws.perm,
-        static_cast<float *>(ws.h), ws.logits, ws.idx, ws.w, ws.counts, ws.inv);
+        static_cast<float *>(ws.h), ws.logits, ws.idx, ws.w, ws.counts, ws.inv,
+        s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
 

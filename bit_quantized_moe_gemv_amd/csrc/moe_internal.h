@@ -27,6 +27,7 @@ constexpr size_t kVqBooksBytes = (size_t)(kVqEntries + kVqResEntries) * 8 * 2;
 struct Shape {
     int H, I, E, K;      // hidden, intermediate, experts, top-k
     int fmt;
+    int routing;         // MOE_ROUTE_*
     size_t expert_bytes;  // bytes of one expert in the packed buffer
     size_t books_bytes;   // bytes before expert 0 (VQ books)
 };
@@ -180,9 +181,9 @@ __device__ __forceinline__ bool key_beats(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-// Selects the k best experts of `l` (E <= 256 logits) and their softmax
-// weights.  Every lane returns the same idx[]/w[]; lane l owns experts l,
-// l+64, l+128, l+192, sorted once by key.  Each round reduces the lanes' heads
+// Selects the k best experts of `l` (E <= 256 logits) and their routing
+// weights (softmax, or normalised sigmoids).  Every lane returns the same
+// idx[]/w[]; lane l owns experts l, l+64, l+128, l+192, sorted once by key.  Each round reduces the lanes' heads
 // to the wave maximum, then to the lowest expert index holding it (both
 // reductions are exact, so the winner does not depend on reduction order); the
 // winning lane pops its head.
@@ -208,7 +209,8 @@ __device__ __forceinline__ void topk_load(const float *__restrict__ l, int E, fl
         if (lane + 64 * j >= E) v[j] = -INFINITY;
 }
 
-__device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, int *idx, float *w) {
+__device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, bool sigmoid,
+                                      int *idx, float *w) {
     const int lane = threadIdx.x & 63;
     float v0 = lv[0], v1 = lv[1], v2 = lv[2], v3 = lv[3];
     int i0 = lane, i1 = lane + 64, i2 = lane + 128, i3 = lane + 192;
@@ -243,12 +245,22 @@ __device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, int *i
             }
         }
     }
-    // softmax over the selected logits (val[0] is the largest)
+    // weights over the selected logits (val[0] is the largest), each first
+    // relative to slot 0's: softmax exp(l_s - l_0); sigmoid
+    // sigma(l_s)/sigma(l_0), as (1 + e^-l0)/(1 + e^-ls) when l_0 > 0 and as
+    // e^(l_s - l_0) (1 + e^l0)/(1 + e^ls) otherwise, so that no exponential
+    // overflows into inf/inf; the ratio of slot 0 is 1, so the sum is >= 1.
     float sum = 0.0f;
+    const float e0n = __expf(-val[0]), e0p = __expf(val[0]);
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) {
         if (s < K) {
-            w[s] = __expf(val[s] - val[0]);
+            const float d = __expf(val[s] - val[0]);
+            float r = d;
+            if (sigmoid)
+                r = val[0] > 0.0f ? (1.0f + e0n) / (1.0f + __expf(-val[s]))
+                                  : d * (1.0f + e0p) / (1.0f + __expf(val[s]));
+            w[s] = s == 0 ? 1.0f : r;
             sum += w[s];
         }
     }
@@ -258,10 +270,11 @@ __device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, int *i
         if (s < K) w[s] *= inv;
 }
 
-__device__ inline void wave_topk(const float *__restrict__ l, int E, int K, int *idx, float *w) {
+__device__ inline void wave_topk(const float *__restrict__ l, int E, int K, bool sigmoid, int *idx,
+                                 float *w) {
     float v[4];
     topk_load(l, E, v);
-    wave_topk_vals(v, E, K, idx, w);
+    wave_topk_vals(v, E, K, sigmoid, idx, w);
 }
 
 // Route positions of a single token: slot s goes to position pos[s], the rank

@@ -128,7 +128,8 @@ constexpr int kRouteThreads = 1024;
 __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     const float *__restrict__ logits, int T, int E, int K, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+    int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    bool sigmoid) {
     __shared__ int s_idx[kDecodeMaxTokens * kMaxTopK];
     __shared__ int s_wtot[kRouteThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     for (int t = wave; t < T; t += nw) {
         int idx[kMaxTopK];
         float w[kMaxTopK];
-        wave_topk(logits + (size_t)t * E, E, K, idx, w);
+        wave_topk(logits + (size_t)t * E, E, K, sigmoid, idx, w);
         if (lane < K) {
             int iv = idx[0];
             float wv = w[0];
@@ -250,7 +251,7 @@ hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const fl
     if (e != hipSuccess || (T == 1 && !route_single)) return e;
     route_small_kernel<<<1, kRouteThreads, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
                                                     ws.counts, ws.offsets, ws.active, ws.perm,
-                                                    ws.inv);
+                                                    ws.inv, s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
 
@@ -264,12 +265,12 @@ hipError_t launch_router(const Shape &s, const uint16_t *x, const float *wr, int
 // one wave per token (prefill)
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T, int E,
                                                    int K, int32_t *__restrict__ idx_out,
-                                                   float *__restrict__ w_out) {
+                                                   float *__restrict__ w_out, bool sigmoid) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     int idx[kMaxTopK];
     float w[kMaxTopK];
-    wave_topk(logits + (size_t)t * E, E, K, idx, w);
+    wave_topk(logits + (size_t)t * E, E, K, sigmoid, idx, w);
     const int lane = threadIdx.x & 63;
     if (lane < K) {
         int iv = idx[0];
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }
 
 hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t st) {
-    topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w);
+    topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
+                                             s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
 

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     int I, int E, int K, const float *__restrict__ logits, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-    float *__restrict__ h) {
+    float *__restrict__ h, bool sigmoid) {
     constexpr int NJ = NSL * TJ;
     constexpr int NWA = NSL * (kVdGroups / GW);  // waves with work
     static_assert(kVdGroups % GW == 0 && NWA <= kVdWaves, "wave split");
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         topk_load(logits, E, lv);
         int sel[kMaxTopK], pos[kMaxTopK];
         float wt[kMaxTopK];
-        wave_topk_vals(lv, E, K, sel, wt);
+        wave_topk_vals(lv, E, K, sigmoid, sel, wt);
         single_token_positions(sel, K, pos);
         int e0 = sel[0];
 #pragma unroll
@@ -395,7 +395,8 @@ static hipError_t vd_gateup_launch(const Shape &s, const uint16_t *x, const uint
     const int grid = s.K * (s.I / 16) / kVdPairs;
     vq_dec_gateup<GW, TJ, NSL><<<grid, kVdThreads, 0, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.logits, ws.idx, ws.w, ws.counts,
-        ws.offsets, ws.active, ws.perm, ws.inv, static_cast<float *>(ws.h));
+        ws.offsets, ws.active, ws.perm, ws.inv, static_cast<float *>(ws.h),
+        s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
 

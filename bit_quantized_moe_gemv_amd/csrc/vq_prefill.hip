@@ -142,28 +142,28 @@ __device__ __forceinline__ void gather_a(const uint32_t (&c)[6], const VqLds &ld
     rbv = lds.rb[i8];
 }
 
-// One sub-step (two K steps) of a wave: 2 x 4 groups x 4 token tiles MFMAs.
-template <int U>
+// One sub-step (two K steps) of a wave: 2 x 4 groups x NTT token tiles MFMAs.
+template <int U, int NTT>
 __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], const VqLds &lds,
-                                           int slot, int lane, f32x4 (&acc)[kVqGroups][4]) {
+                                           int slot, int lane, f32x4 (&acc)[kVqGroups][NTT]) {
     const int q = lane >> 4, n = lane & 15;
     uint4 cb0[kVqGroups], rb0[kVqGroups], cb1[kVqGroups], rb1[kVqGroups];
-    uint4 b0[4], b1[4];
+    uint4 b0[NTT], b1[NTT];
 #pragma unroll
     for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U>(cr[g], lds, cb0[g], rb0[g]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTT; ++t)
         b0[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][0][q][16 * t + n]);
 #pragma unroll
     for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U + 1>(cr[g], lds, cb1[g], rb1[g]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTT; ++t)
         b1[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][1][q][16 * t + n]);
     f16x8 a0[kVqGroups];
 #pragma unroll
     for (int g = 0; g < kVqGroups; ++g) a0[g] = add_f16x8(cb0[g], rb0[g]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTT; ++t)
 #pragma unroll
         for (int g = 0; g < kVqGroups; ++g)
             acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -172,7 +172,7 @@ __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], c
 #pragma unroll
     for (int g = 0; g < kVqGroups; ++g) a1[g] = add_f16x8(cb1[g], rb1[g]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTT; ++t)
 #pragma unroll
         for (int g = 0; g < kVqGroups; ++g)
             acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -186,12 +186,20 @@ __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], c
 // lane); MODE 0 slices are 256 gate rows with their up partners (wave w: gate
 // groups 16b+2w, +1 and the two up partners), MODE 1 slices are 512 output
 // rows (wave w: groups 32b+4w..+3, clamped past the end and never stored).
+// NTT = 4: 64-token chunks over all E experts.  NTT = 1 (batches of at most
+// 16 tokens, so at most 16 routes per expert): one 16-token chunk per item,
+// and the items run over the active experts only (the list the small-batch
+// routing writes), so no MFMA works on absent tokens or experts.
 // ---------------------------------------------------------------------------
-template <int MODE>
+template <int MODE, int NTT>
 __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int E,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-    const uint16_t *__restrict__ bsrc, const int32_t *__restrict__ bexp, float *__restrict__ out) {
+    const int32_t *__restrict__ active, const uint16_t *__restrict__ bsrc,
+    const int32_t *__restrict__ bexp, float *__restrict__ out) {
+    constexpr bool kSmall = NTT == 1;
+    constexpr int kChunk = 16 * NTT;                   // tokens per chunk
+    constexpr int kLanes = kSmall ? 1 : kVqChunkLanes;  // items per (expert, slice)
     __shared__ __align__(16) VqLds lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const int NJ = NK / 256;                 // super-steps
     const int NS = 4 * NJ;                   // sub-steps
     const int nslice = MODE == 0 ? I / 256 : (H + 511) / 512;
-    const int per_e = nslice * kVqChunkLanes;
+    const int per_e = nslice * kLanes;
     const size_t nvec = (size_t)NROW * NK / 8;
     size_t mat_off = 0;
     if (MODE == 1) {
@@ -220,16 +228,16 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     // blockIdx -> items: with E and the grid multiples of 8, the blocks of one
     // XCD (the dispatcher deals blocks round-robin over the 8 XCDs) take the
     // experts e = xcd (mod 8), so an expert's token rows stay in one L2.
-    const bool by_xcd = (E & 7) == 0 && (gridDim.x & 7) == 0;
+    const bool by_xcd = !kSmall && (E & 7) == 0 && (gridDim.x & 7) == 0;
     const int xcd = by_xcd ? (int)(blockIdx.x & 7) : 0;
     const int first = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
     const int stride = by_xcd ? (int)(gridDim.x >> 3) : (int)gridDim.x;
-    const int items = by_xcd ? (E >> 3) * per_e : E * per_e;
+    const int items = kSmall ? active[0] * per_e : by_xcd ? (E >> 3) * per_e : E * per_e;
 
     for (int it = first; it < items; it += stride) {
-        const int e = by_xcd ? xcd + 8 * (it / per_e) : it / per_e;
+        const int e = kSmall ? active[1 + it / per_e] : by_xcd ? xcd + 8 * (it / per_e) : it / per_e;
         const int rest = it % per_e;
-        const int slice = rest / kVqChunkLanes, chl = rest % kVqChunkLanes;
+        const int slice = rest / kLanes, chl = rest % kLanes;
         const int p0 = offsets[e];
         const int ne = offsets[e + 1] - p0;
         const uint8_t *mat = packed + kVqBooksBytes + (size_t)e * expert_bytes + mat_off;
@@ -247,17 +255,17 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                 grp[g] = min(32 * slice + 4 * wave + g, H / 16 - 1);
         }
 
-        for (int c0 = 64 * chl; c0 < ne; c0 += 64 * kVqChunkLanes) {
-            const int nt = min(64, ne - c0);
+        for (int c0 = kChunk * chl; c0 < ne; c0 += kChunk * kLanes) {
+            const int nt = min(kChunk, ne - c0);
             const int pr = p0 + c0 + min(lane, nt - 1);
             const uint16_t *brow =
                 MODE == 0 ? bsrc + (size_t)(perm[pr] / K) * H : bsrc + (size_t)pr * I;
 
-            f32x4 acc[kVqGroups][4];
+            f32x4 acc[kVqGroups][NTT];
 #pragma unroll
             for (int g = 0; g < kVqGroups; ++g)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < NTT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
             uint32_t cr[2][kVqGroups][6];
             auto issue_codes = [&](int slot, int J) {
@@ -319,10 +327,10 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                         if (u == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
                         if (J < NJ) {
                             const int slot = S % kVqRing;
-                            if (u == 0) vq_substep<0>(cr[jj], lds, slot, lane, acc);
-                            if (u == 1) vq_substep<1>(cr[jj], lds, slot, lane, acc);
-                            if (u == 2) vq_substep<2>(cr[jj], lds, slot, lane, acc);
-                            if (u == 3) vq_substep<3>(cr[jj], lds, slot, lane, acc);
+                            if (u == 0) vq_substep<0, NTT>(cr[jj], lds, slot, lane, acc);
+                            if (u == 1) vq_substep<1, NTT>(cr[jj], lds, slot, lane, acc);
+                            if (u == 2) vq_substep<2, NTT>(cr[jj], lds, slot, lane, acc);
+                            if (u == 3) vq_substep<3, NTT>(cr[jj], lds, slot, lane, acc);
                         }
                     }
                 }
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
 
             // epilogue: lane holds rows 4q..4q+3 of each group for token 16t+n
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < NTT; ++t) {
                 const int m = 16 * t + n;
                 if (m >= nt) continue;
                 const int p = p0 + c0 + m;
@@ -383,15 +391,27 @@ static int vq_grid(int items) {
     return max(g, 1);
 }
 
+template <int MODE, int NTT>
+static void vq_launch(const Shape &s, int items, const uint8_t *packed, const Workspace &ws,
+                      const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
+    vq_prefill_kernel<MODE, NTT><<<vq_grid(items), kVqThreads, 0, st>>>(
+        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.active, bsrc, bexp,
+        out);
+}
+
+// Batches of at most kDecodeMaxTokens tokens (routed by the small-batch
+// routing, which lists the active experts) take the one-tile variant.
 hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
                                     const uint8_t *packed, const Workspace &ws, hipStream_t st) {
     vq_xpack_kernel<<<T, 256, 0, st>>>(x, s.H, ws.x16, ws.xexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int items = s.E * (s.I / 256) * kVqChunkLanes;
-    vq_prefill_kernel<0><<<vq_grid(items), kVqThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.x16, ws.xexp,
-        static_cast<float *>(ws.h));
+    const int ns = s.I / 256;
+    float *h = static_cast<float *>(ws.h);
+    if (T <= kDecodeMaxTokens)
+        vq_launch<0, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.x16, ws.xexp, h, st);
+    else
+        vq_launch<0, 4>(s, s.E * ns * kVqChunkLanes, packed, ws, ws.x16, ws.xexp, h, st);
     return hipGetLastError();
 }
 
@@ -401,9 +421,11 @@ hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
                                              ws.hexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int items = s.E * ((s.H + 511) / 512) * kVqChunkLanes;
-    vq_prefill_kernel<1><<<vq_grid(items), kVqThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.h16, ws.hexp, ws.y);
+    const int ns = (s.H + 511) / 512;
+    if (T <= kDecodeMaxTokens)
+        vq_launch<1, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.h16, ws.hexp, ws.y, st);
+    else
+        vq_launch<1, 4>(s, s.E * ns * kVqChunkLanes, packed, ws, ws.h16, ws.hexp, ws.y, st);
     return hipGetLastError();
 }
 

@@ -89,6 +89,15 @@ enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2 };
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 #define MOE_DECODE_MAX_TOKENS 16
 
+/* Routing weights over a token's k selected experts (the selection itself is
+ * the same top-k of the logits either way):
+ *   MOE_ROUTE_SOFTMAX  w_s = exp(l_s) / sum_j exp(l_j)
+ *   MOE_ROUTE_SIGMOID  w_s = sigma(l_s) / sum_j sigma(l_j), sigma(l) = 1/(1+e^-l)
+ * (the TrevorJS card, "Architecture notes", lists sigmoid routing for MiMo;
+ * neither form applies an extra scale).  Both are computed in fp32 in a form
+ * that stays finite for every finite logit. */
+enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_SIGMOID = 1 };
+
 typedef struct {
     int32_t hidden;     /* H: multiple of 256 */
     int32_t inter;      /* I: multiple of 128 (MXFP4) or 256 (VQ13R8) */
@@ -97,6 +106,7 @@ typedef struct {
     int32_t max_tokens; /* largest T a forward call may pass: 1..65536 */
     int32_t format;     /* MOE_FMT_* */
     int32_t force_path; /* MOE_PATH_* */
+    int32_t routing;    /* MOE_ROUTE_* (0, the zero-initialised value, is softmax) */
 } moe_layer_desc;
 
 /* Size in bytes of packed_experts for this descriptor (host out-pointer). */

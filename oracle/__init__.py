@@ -66,13 +66,13 @@ def _load():
         lib.oracle_router_logits_f64.restype = _INT
         lib.oracle_router_logits_f64.argtypes = [_P, _P, _I64, _I64, _I64, _P]
         lib.oracle_topk.restype = _INT
-        lib.oracle_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        lib.oracle_topk.argtypes = [_P, _I64, _I64, _I64, _INT, _P, _P]
         lib.oracle_permute.restype = _INT
         lib.oracle_permute.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
         lib.oracle_expert_ffn.restype = _INT
         lib.oracle_expert_ffn.argtypes = [_INT, _I64, _I64, _I64, _P, _I64, _P, _P, _P]
         lib.oracle_moe_forward.restype = _INT
-        lib.oracle_moe_forward.argtypes = [_INT, _I64, _I64, _I64, _I64, _P, _P, _P, _I64,
+        lib.oracle_moe_forward.argtypes = [_INT, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _I64,
                                            _P, _I64, _P, _P, _P, _P]
         _lib = lib
     return _lib
@@ -142,12 +142,17 @@ def router_logits_f64(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     return out
 
 
-def topk(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+ROUTE_SOFTMAX = 0
+ROUTE_SIGMOID = 1
+
+
+def topk(logits: np.ndarray, k: int, routing: int = ROUTE_SOFTMAX) -> tuple[np.ndarray, np.ndarray]:
+    """Top-k experts per token and their weights (softmax, or sigmoid routing)."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     t, e = logits.shape
     idx = np.empty((t, k), dtype=np.int32)
     w = np.empty((t, k), dtype=np.float64)
-    _check(_load().oracle_topk(_ptr(logits), t, e, k, _ptr(idx), _ptr(w)), "topk")
+    _check(_load().oracle_topk(_ptr(logits), t, e, k, routing, _ptr(idx), _ptr(w)), "topk")
     return idx, w
 
 
@@ -164,10 +169,10 @@ def permute(idx: np.ndarray, experts: int):
     return counts, offsets, perm, inv
 
 
-def route(x: np.ndarray, wr: np.ndarray, k: int):
+def route(x: np.ndarray, wr: np.ndarray, k: int, routing: int = ROUTE_SOFTMAX):
     """Logits, top-k and grouping for all tokens: dict of numpy arrays."""
     logits = router_logits(x, wr)
-    idx, w = topk(logits, k)
+    idx, w = topk(logits, k, routing)
     counts, offsets, perm, inv = permute(idx, wr.shape[0])
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv)
 
@@ -183,7 +188,8 @@ def expert_ffn(fmt: int, hidden: int, inter: int, experts: int, packed: np.ndarr
 
 
 def moe_forward(fmt: int, hidden: int, inter: int, experts: int, top_k: int,
-                packed: np.ndarray, x: np.ndarray, wr: np.ndarray, tokens=None):
+                packed: np.ndarray, x: np.ndarray, wr: np.ndarray, tokens=None,
+                routing: int = ROUTE_SOFTMAX):
     """Layer output for the listed tokens (all when None).
 
     Returns dict(out [n,H] float64, idx [n,k] int32, w [n,k] float64,
@@ -201,7 +207,7 @@ def moe_forward(fmt: int, hidden: int, inter: int, experts: int, top_k: int,
     idx = np.empty((n, top_k), dtype=np.int32)
     w = np.empty((n, top_k), dtype=np.float64)
     logits = np.empty((n, experts), dtype=np.float32)
-    _check(_load().oracle_moe_forward(fmt, hidden, inter, experts, top_k, _ptr(packed), _ptr(x),
+    _check(_load().oracle_moe_forward(fmt, hidden, inter, experts, top_k, routing, _ptr(packed), _ptr(x),
                                       _ptr(wr), t, _ptr(tok), n, _ptr(out), _ptr(idx), _ptr(w),
                                       _ptr(logits)), "moe_forward")
     return dict(out=out, idx=idx, w=w, logits=logits, tokens=tok)
@@ -209,4 +215,5 @@ def moe_forward(fmt: int, hidden: int, inter: int, experts: int, top_k: int,
 
 def workload_forward(wl, packed, x, wr, tokens=None):
     """moe_forward with the shapes of a workloads.Workload."""
-    return moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, packed, x, wr, tokens)
+    return moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, packed, x, wr, tokens,
+                       routing=wl.routing)

@@ -13,7 +13,8 @@
  *
  *   l[e]   = sum_h x[t,h] * Wr[e,h]                 (fp32, canonical order)
  *   idx    = the k experts with the largest l, ties to the lower index
- *   w[s]   = softmax over the k selected logits      (double)
+ *   w[s]   = softmax over the k selected logits      (double), or, with
+ *            sigmoid routing, sigma(l_s) / sum_j sigma(l_j) over them
  *   h_s[i] = silu(G_e[i,:] x) * (U_e[i,:] x)         (double)
  *   y_s[j] = D_e[j,:] h_s                            (double)
  *   out[t] = sum_{s<k} w[s] * y_s, in slot order     (double)
@@ -27,6 +28,9 @@
  *
  * Readings taken where the pages are silent (each is pinned by a test):
  *  - routing weights are a softmax over the k selected logits, no extra scale;
+ *    the TrevorJS card ("Architecture notes") names sigmoid routing for MiMo,
+ *    read as the same selection with weights sigma(l_s) normalised over the
+ *    k selected experts, again with no extra scale;
  *  - the fp32 router logit is summed in the canonical order of
  *    oracle_router_logits so that routing can be compared bit for bit;
  *  - ties between equal logits go to the lower expert index;
@@ -259,13 +263,27 @@ int oracle_router_logits_f64(const uint16_t *x, const float *wr, int64_t T, int6
     return 0;
 }
 
+/* The logistic function in double, evaluated on the side where exp() cannot
+ * overflow: 1/(1+e^-v) for v >= 0, e^v/(1+e^v) for v < 0. */
+static double or_sigmoid(double v) {
+    if (v >= 0.0) return 1.0 / (1.0 + exp(-v));
+    const double z = exp(v);
+    return z / (1.0 + z);
+}
+
 /* Top-k selection: repeatedly take the unselected expert with the largest
  * logit; a strict comparison keeps the lower index on equal logits (so -0 and
- * +0 tie).  Slots are ordered by (logit descending, index ascending).  Weights:
- * softmax over the k selected logits, in double.  (8 active experts per token
- * -- TrevorJS card, "Architecture notes"; "eight routes per processed token"
- * -- ProCreations IQ3 card, "Calibration".) */
-int oracle_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *idx, double *w) {
+ * +0 tie).  Slots are ordered by (logit descending, index ascending).  Weights,
+ * in double: routing 0, softmax over the k selected logits; routing 1 (sigmoid
+ * routing -- TrevorJS card, "Architecture notes"), sigma(l_s) divided by the
+ * sum of sigma over the k selected logits.  (The logistic form is used for
+ * logits above -700; below that every sigma underflows in double and the
+ * ratio is undefined here.)  (8 active experts per token -- TrevorJS card,
+ * "Architecture notes"; "eight routes per processed token" -- ProCreations IQ3
+ * card, "Calibration".) */
+int oracle_topk(const float *logits, int64_t T, int64_t E, int64_t k, int routing, int32_t *idx,
+                double *w) {
+    if (routing != 0 && routing != 1) return -1;
     if (k < 1 || k > E) return -1;
     for (int64_t t = 0; t < T; t++) {
         const float *l = logits + t * E;
@@ -279,10 +297,17 @@ int oracle_topk(const float *logits, int64_t T, int64_t E, int64_t k, int32_t *i
             idx[t * k + s] = (int32_t)best;
         }
         free(taken);
-        double m = (double)l[idx[t * k]];
-        double sum = 0.0;
-        for (int64_t s = 0; s < k; s++) sum += exp((double)l[idx[t * k + s]] - m);
-        for (int64_t s = 0; s < k; s++) w[t * k + s] = exp((double)l[idx[t * k + s]] - m) / sum;
+        if (routing == 0) {
+            double m = (double)l[idx[t * k]];
+            double sum = 0.0;
+            for (int64_t s = 0; s < k; s++) sum += exp((double)l[idx[t * k + s]] - m);
+            for (int64_t s = 0; s < k; s++) w[t * k + s] = exp((double)l[idx[t * k + s]] - m) / sum;
+        } else {
+            double sum = 0.0;
+            for (int64_t s = 0; s < k; s++) sum += or_sigmoid((double)l[idx[t * k + s]]);
+            for (int64_t s = 0; s < k; s++)
+                w[t * k + s] = or_sigmoid((double)l[idx[t * k + s]]) / sum;
+        }
     }
     return 0;
 }
@@ -358,8 +383,9 @@ int oracle_expert_ffn(int fmt, int64_t H, int64_t I, int64_t E, const uint8_t *p
 }
 
 /* The whole layer for the listed tokens (all tokens when tokens == NULL):
- * out [n][H] double, idx [n][k], w [n][k] double, logits [n][E] fp32. */
-int oracle_moe_forward(int fmt, int64_t H, int64_t I, int64_t E, int64_t k,
+ * out [n][H] double, idx [n][k], w [n][k] double, logits [n][E] fp32.
+ * routing: 0 softmax, 1 sigmoid (see oracle_topk). */
+int oracle_moe_forward(int fmt, int64_t H, int64_t I, int64_t E, int64_t k, int routing,
                        const uint8_t *packed, const uint16_t *x, const float *wr, int64_t T,
                        const int64_t *tokens, int64_t n, double *out, int32_t *idx, double *w,
                        float *logits) {
@@ -378,7 +404,7 @@ int oracle_moe_forward(int fmt, int64_t H, int64_t I, int64_t E, int64_t k,
         if (t < 0 || t >= T) { rc = -1; break; }
         const uint16_t *xt = x + t * H;
         rc = oracle_router_logits(xt, wr, 1, H, E, logits + q * E);
-        if (rc == 0) rc = oracle_topk(logits + q * E, 1, E, k, idx + q * k, w + q * k);
+        if (rc == 0) rc = oracle_topk(logits + q * E, 1, E, k, routing, idx + q * k, w + q * k);
         if (rc != 0) break;
         for (int64_t kk = 0; kk < H; kk++) xd[kk] = oracle_bf16(xt[kk]);
         double *o = out + q * H;

@@ -35,7 +35,7 @@ class Runner:
         self.wl = wl
         self.bq = bq
         self.layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k,
-                                 max_tokens or wl.tokens, wl.fmt, force_path)
+                                 max_tokens or wl.tokens, wl.fmt, force_path, routing=wl.routing)
         self.packed_host = W.make_experts(wl) if packed is None else packed
         self.packed = torch.from_numpy(self.packed_host).to("cuda")
         self.torch = torch

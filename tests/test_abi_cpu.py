@@ -140,3 +140,13 @@ def test_vq_descriptor_sizes_and_paths(lib):
     r = 2048 * 8
     assert vq - mx >= 2048 * 4096 * 2 + r * 2048 * 2 + (2048 + r) * 4
     assert vq - mx < 2048 * 4096 * 2 + r * 2048 * 2 + (2048 + r) * 4 + 4 * 256
+
+
+def test_routing_field_validated(lib):
+    """routing 0 (softmax) and 1 (sigmoid) are accepted; other values are not."""
+    for r in (bq.MOE_ROUTE_SOFTMAX, bq.MOE_ROUTE_SIGMOID):
+        assert bq.workspace_size(256, 128, 8, 2, 16, routing=r) > 0
+    for r in (-1, 2, 7):
+        with pytest.raises(bq.MoeError) as ei:
+            bq.workspace_size(256, 128, 8, 2, 16, routing=r)
+        assert ei.value.status == bq.MOE_EINVAL

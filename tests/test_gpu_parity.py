@@ -43,9 +43,9 @@ def _full_check(torch_dev, wl, path, x=None, wr=None, packed=None, max_tokens=No
     wr = W.make_router(wl) if wr is None else wr
     run = Runner(wl, path, max_tokens=max_tokens or x.shape[0], packed=packed)
     got = run.run(x, wr)
-    ref_route = oracle.route(x, wr, wl.top_k)
+    ref_route = oracle.route(x, wr, wl.top_k, wl.routing)
     ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k,
-                             run.packed_host, x, wr)
+                             run.packed_host, x, wr, routing=wl.routing)
     assert got["path"] == path
     _routing_exact(got, ref_route, wl)
     l2, mx = check_output(got["out"], ref["out"])
@@ -133,11 +133,11 @@ def _sampled_check(torch_dev, wl, path, sample):
     run = Runner(wl, path, packed=packed)
     got = run.run(x, wr)
     log("  gpu done; oracle routing")
-    ref_route = oracle.route(x, wr, wl.top_k)
+    ref_route = oracle.route(x, wr, wl.top_k, wl.routing)
     _routing_exact(got, ref_route, wl)
     log("  routing exact; oracle outputs")
     ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, packed, x, wr,
-                             tokens=sample)
+                             tokens=sample, routing=wl.routing)
     l2, mx = check_output(got["out"][np.asarray(sample)], ref["out"])
     log(f"  worst sampled row: rel l2 {l2:.2e}, max/rms {mx:.2e}")
     assert np.all(np.isfinite(got["out"]))
@@ -189,3 +189,31 @@ def test_replay_stage_reproduces_forward(torch_dev, path):
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
     if path == DEC:
         assert layer.replay_stage_raw("combine", 1, *args) == bq.MOE_EINVAL
+
+
+SIGMOID = 1
+
+
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+@pytest.mark.parametrize("t", [1, 5, 16])
+def test_sigmoid_routing_tiny(torch_dev, path, t):
+    """Sigmoid routing weights (same selection, weights sigma(l)/sum sigma)."""
+    wl = W.TINY.replace(tokens=t, seed=300 + t, routing=SIGMOID)
+    _full_check(torch_dev, wl, path)
+
+
+def test_sigmoid_routing_prefill_large_batch(torch_dev):
+    _full_check(torch_dev, W.TINY.replace(tokens=200, seed=310, routing=SIGMOID), PRE)
+
+
+def test_sigmoid_routing_extreme_logits(torch_dev):
+    """Router rows scaled so that logits reach about +-1e3: the weights stay
+    finite and match the oracle (every sigma is 0 or 1 in fp32 there)."""
+    wl = W.TINY.replace(tokens=16, seed=311, routing=SIGMOID, router_std=20.0)
+    for path in (DEC, PRE):
+        got, _, _ = _full_check(torch_dev, wl, path)
+        assert np.all(np.isfinite(got["w"]))
+
+
+def test_mimo_decode_batch1_sigmoid(torch_dev):
+    _sampled_check(torch_dev, W.DECODE.replace(routing=SIGMOID), DEC, [0])

@@ -128,3 +128,9 @@ def test_mimo_vq_decode_batch1(torch_dev):
                              run.packed_host, x, wr)
     l2, mx = check_output(got["out"], ref["out"])
     log(f"  rel l2 {l2:.2e}, max/rms {mx:.2e}")
+
+
+def test_vq_decode_sigmoid_routing(torch_dev):
+    for seed in (70, 71):
+        _full_check(torch_dev, W.TINY_VQ.replace(tokens=1, seed=seed, top_k=8, routing=1), DEC)
+    _full_check(torch_dev, W.TINY_VQ.replace(tokens=9, seed=72, routing=1), PRE)

@@ -188,3 +188,55 @@ def test_skewed_verify_routing_concentrates_on_hot_experts(oracle_lib):
     hot = set(W.hot_expert_ids(wl).tolist())
     frac = np.isin(idx, list(hot)).mean()
     assert 0.45 < frac < 0.55, frac
+
+
+# --- sigmoid routing: same selection, weights sigma(l_s) / sum_j sigma(l_j)
+# over the selected logits (TrevorJS card, "Architecture notes").
+
+def test_sigmoid_routing_selects_like_softmax_and_sums_to_one(oracle_lib):
+    rng = np.random.default_rng(21)
+    l = rng.normal(0.0, 3.0, size=(40, 256)).astype(np.float32)
+    i_soft, _ = oracle_lib.topk(l, 8, oracle_lib.ROUTE_SOFTMAX)
+    i_sig, w_sig = oracle_lib.topk(l, 8, oracle_lib.ROUTE_SIGMOID)
+    assert np.array_equal(i_soft, i_sig)  # sigma is increasing
+    assert np.allclose(w_sig.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(w_sig, axis=1) <= 0)  # slot order = weight order
+
+
+def test_sigmoid_routing_symmetric_pair_is_sigma(oracle_lib):
+    """Two selected logits a and -a: sigma(a) + sigma(-a) = 1, so the first
+    weight is sigma(a) = (1 + tanh(a/2)) / 2 (checked with tanh)."""
+    for a in (0.25, 1.0, 3.5, 12.0):
+        l = np.array([[a, -a, -40.0]], dtype=np.float32)
+        idx, w = oracle_lib.topk(l, 2, oracle_lib.ROUTE_SIGMOID)
+        assert idx[0].tolist() == [0, 1]
+        assert w[0, 0] == pytest.approx((1.0 + np.tanh(a / 2.0)) / 2.0, rel=1e-14)
+        assert w[0, 1] == pytest.approx((1.0 - np.tanh(a / 2.0)) / 2.0, rel=1e-12)
+
+
+def test_sigmoid_routing_limits(oracle_lib):
+    """Far below zero sigma(l) = e^l (1 - e^l + ...), so the weights approach
+    the softmax over the same logits; far above zero every sigma is 1 to
+    within e^-l, so the weights approach 1/k.  Zero logits give exactly 1/k."""
+    rng = np.random.default_rng(22)
+    base = rng.normal(0.0, 1.0, size=(8, 64)).astype(np.float32)
+    _, w_soft = oracle_lib.topk(base - 60.0, 8, oracle_lib.ROUTE_SOFTMAX)
+    _, w_low = oracle_lib.topk(base - 60.0, 8, oracle_lib.ROUTE_SIGMOID)
+    # e^-60 ~ 1e-26 is far below double rounding: agreement to rounding
+    assert np.max(np.abs(w_low - w_soft) / w_soft) < 1e-13
+    _, w_high = oracle_lib.topk(base + 60.0, 8, oracle_lib.ROUTE_SIGMOID)
+    assert np.max(np.abs(w_high - 1.0 / 8.0)) < 1e-15
+    _, w_zero = oracle_lib.topk(np.zeros((3, 16), dtype=np.float32), 4,
+                                oracle_lib.ROUTE_SIGMOID)
+    assert np.all(w_zero == 0.25)
+
+
+def test_sigmoid_routing_differs_from_softmax_in_between(oracle_lib):
+    """Near zero the two weightings differ: logits (1, 0) give softmax
+    e/(e+1) ~ 0.731 but sigmoid weights sigma(1)/(sigma(1)+1/2) ~ 0.594."""
+    l = np.array([[1.0, 0.0]], dtype=np.float32)
+    _, w_soft = oracle_lib.topk(l, 2, oracle_lib.ROUTE_SOFTMAX)
+    _, w_sig = oracle_lib.topk(l, 2, oracle_lib.ROUTE_SIGMOID)
+    s1 = (1.0 + np.tanh(0.5)) / 2.0
+    assert w_soft[0, 0] == pytest.approx(np.e / (np.e + 1.0), rel=1e-14)
+    assert w_sig[0, 0] == pytest.approx(s1 / (s1 + 0.5), rel=1e-14)

@@ -132,6 +132,8 @@ class Workload:
     scaled_tokens: int = 0
     token_scale: float = 1.0
     router_std: float = 0.02
+    # routing weights: 0 softmax over the selected logits, 1 normalised sigmoids
+    routing: int = 0
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
