@@ -131,6 +131,17 @@ class Bench:
             torch.cuda.synchronize()
         return self._vq
 
+    def vq13_layers(self):
+        """One device copy of the VQ13 layer (1.3 GB: larger than every cache)."""
+        if not hasattr(self, "_vq13"):
+            W, torch = self.W, self.torch
+            log(f"generating the MiMo-shaped VQ13 layer ({W.VQ13_DECODE.packed_bytes} B)")
+            host = W.make_experts(W.VQ13_DECODE)
+            self._vq13 = self._copies(host, 1)
+            del host
+            torch.cuda.synchronize()
+        return self._vq13
+
     def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0):
         torch, bq, W = self.torch, self.bq, self.W
         T = tokens_per_step
@@ -342,6 +353,9 @@ def main():
         vqv = b.run(W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed"), 100, 10,
                     16, layers=b.vq_layers(), replay=20)
         extra["vq_verify_t16"] = vqv
+        log("VQ13 decode T=1")
+        extra["vq13_decode_t1"] = b.run(W.VQ13_DECODE, 200, 20, 1, layers=b.vq13_layers(),
+                                        replay=100)
         log("VQ13R8 prefill T=2048")
         vq = b.run(W.VQ_PREFILL, 30, 5, 2048, layers=b.vq_layers(), replay=10)
         extra["vq_prefill_t2048"] = prefill_report(

@@ -24,6 +24,7 @@ MOE_EHIP = -4
 
 MOE_FMT_MXFP4 = 1
 MOE_FMT_VQ13R8 = 2
+MOE_FMT_VQ13 = 3
 
 MOE_PATH_AUTO = 0
 MOE_PATH_DECODE = 1

@@ -61,7 +61,7 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256(R * 4);                   // inv
     b += align256(R * s.I * 4);             // h
     b += align256(R * s.H * 4);             // y
-    if (s.fmt == MOE_FMT_VQ13R8) {
+    if (is_vq_format(s.fmt)) {
         b += align256((size_t)tmax * s.H * 2);  // x16
         b += align256((size_t)tmax * 4);        // xexp
         b += align256(R * s.I * 2);             // h16
@@ -92,7 +92,7 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->xexp = nullptr;
     ws->h16 = nullptr;
     ws->hexp = nullptr;
-    if (s.fmt == MOE_FMT_VQ13R8) {
+    if (is_vq_format(s.fmt)) {
         ws->x16 = reinterpret_cast<uint16_t *>(take((size_t)tmax * s.H * 2));
         ws->xexp = reinterpret_cast<int32_t *>(take((size_t)tmax * 4));
         ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
@@ -113,7 +113,7 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
     if (d->routing != MOE_ROUTE_SOFTMAX && d->routing != MOE_ROUTE_SIGMOID) return MOE_EINVAL;
     if (d->format == MOE_FMT_MXFP4) {
         if (d->inter % 128) return MOE_EINVAL;
-    } else if (d->format == MOE_FMT_VQ13R8) {
+    } else if (is_vq_format(d->format)) {
         if (d->inter % 256) return MOE_EINVAL;
     } else {
         return MOE_EINVAL;
@@ -129,9 +129,12 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
         if (d->format == MOE_FMT_MXFP4) {
             s->expert_bytes = 3 * I * H * 17 / 32;
             s->books_bytes = 0;
-        } else {
+        } else if (d->format == MOE_FMT_VQ13R8) {
             s->expert_bytes = 3 * I * H * 21 / 64 + 2 * (2 * I + H);
             s->books_bytes = kVqBooksBytes;
+        } else {
+            s->expert_bytes = 3 * I * H * 13 / 64 + 2 * (2 * I + H);
+            s->books_bytes = kVq13BooksBytes;
         }
     }
     // the decode kernels are instantiated for power-of-two widths
@@ -234,7 +237,7 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
                 err = staged(L, slot, MOE_STAGE_PERMUTE, st,
                              [&] { return launch_permute(s, T, ws, st); });
         }
-        const bool vq = s.fmt == MOE_FMT_VQ13R8;
+        const bool vq = is_vq_format(s.fmt);
         if (err == hipSuccess)
             err = staged(L, slot, MOE_STAGE_GATEUP, st, [&] {
                 return vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
@@ -290,7 +293,7 @@ int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void
     const Shape &s = L->shape;
     const Workspace &ws = L->ws;
     const int T = L->last_T;
-    const bool vq = s.fmt == MOE_FMT_VQ13R8;
+    const bool vq = is_vq_format(s.fmt);
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
     for (int i = 0; i < reps; ++i) {

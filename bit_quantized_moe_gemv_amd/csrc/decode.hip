@@ -359,18 +359,18 @@ static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
 }
 
 bool decode_supported(const Shape &s) {
-    if (s.fmt == MOE_FMT_VQ13R8) return vq_decode_supported(s);
+    if (is_vq_format(s.fmt)) return vq_decode_supported(s);
     const int nj = s.H / 256;
     const bool h_ok = nj == 1 || nj == 2 || nj == 4 || nj == 8 || nj == 16 || nj == 32;
     const bool i_ok = s.I == 128 || s.I == 256 || s.I == 512 || s.I == 1024 || s.I == 2048;
     return s.fmt == MOE_FMT_MXFP4 && h_ok && i_ok;
 }
 
-int decode_max_tokens(const Shape &s) { return s.fmt == MOE_FMT_VQ13R8 ? 1 : kDecodeMaxTokens; }
+int decode_max_tokens(const Shape &s) { return is_vq_format(s.fmt) ? 1 : kDecodeMaxTokens; }
 
 hipError_t launch_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
-    if (s.fmt == MOE_FMT_VQ13R8) return launch_vq_decode_gateup(s, T, x, packed, ws, st);
+    if (is_vq_format(s.fmt)) return launch_vq_decode_gateup(s, T, x, packed, ws, st);
     switch (s.H / 256) {
         case 1: return gateup_launch_tc<1>(s, T, x, packed, ws, st);
         case 2: return gateup_launch_tc<2>(s, T, x, packed, ws, st);
@@ -393,7 +393,7 @@ static hipError_t down_launch(const Shape &s, int T, const uint8_t *packed, cons
 
 hipError_t launch_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                               float *out, hipStream_t st) {
-    if (s.fmt == MOE_FMT_VQ13R8) return launch_vq_decode_down(s, T, packed, ws, out, st);
+    if (is_vq_format(s.fmt)) return launch_vq_decode_down(s, T, packed, ws, out, st);
     if (s.I > kDnMaxI || T * s.K > kDnMaxR) return hipErrorInvalidValue;
     switch (s.I) {
         case 128:

@@ -21,7 +21,12 @@ constexpr int kMaxExperts = 256;
 constexpr int kDecodeMaxTokens = 16;
 constexpr int kVqEntries = 8192;
 constexpr int kVqResEntries = 256;
-constexpr size_t kVqBooksBytes = (size_t)(kVqEntries + kVqResEntries) * 8 * 2;
+constexpr size_t kVqBooksBytes = (size_t)(kVqEntries + kVqResEntries) * 8 * 2;  // VQ13R8
+constexpr size_t kVq13BooksBytes = (size_t)kVqEntries * 8 * 2;                     // VQ13
+
+__host__ __device__ constexpr bool is_vq_format(int fmt) {
+    return fmt == MOE_FMT_VQ13R8 || fmt == MOE_FMT_VQ13;
+}
 
 // Shapes of one layer.
 struct Shape {

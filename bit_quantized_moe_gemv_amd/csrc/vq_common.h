@@ -1,5 +1,5 @@
-// vq_common.h -- device helpers shared by the VQ13R8 kernels (the packed
-// format is described with MOE_FMT_VQ13R8 in bqmoe.h).
+// vq_common.h -- device helpers shared by the VQ kernels (the packed formats
+// are described with MOE_FMT_VQ13R8 and MOE_FMT_VQ13 in bqmoe.h).
 #pragma once
 
 #include "moe_internal.h"
@@ -51,7 +51,9 @@ __device__ __forceinline__ f16x8 add_f16x8(uint4 a, uint4 b) {
     return __builtin_bit_cast(f16x8, a) + __builtin_bit_cast(f16x8, b);
 }
 
-// Byte regions of one VQ matrix of N rows and K columns.
+// Byte regions of one VQ matrix of N rows and K columns; RES: the matrix
+// carries the residual index region (VQ13R8) or not (VQ13).
+template <bool RES>
 struct VqMatrix {
     const uint8_t *c12, *pln, *res;
     const uint16_t *gain;
@@ -60,25 +62,36 @@ struct VqMatrix {
         c12 = base;
         pln = c12 + nvec * 3 / 2;
         res = pln + nvec / 8;
-        gain = reinterpret_cast<const uint16_t *>(res + nvec);
+        gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
     }
-    // lane's run of tile `tile`: 12 code12 bytes, 8 res bytes, 1 plane byte
+    // lane's run of tile `tile`: 12 code12 bytes, 8 res bytes (zero without
+    // the residual stage), 1 plane byte
     __device__ __forceinline__ void load(size_t tile, int lane, uint32_t (&c)[6]) const {
         const u32x3 a = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
-        const uint2 r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
         c[0] = a.x;
         c[1] = a.y;
         c[2] = a.z;
-        c[3] = r.x;
-        c[4] = r.y;
+        if (RES) {
+            const uint2 r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
+            c[3] = r.x;
+            c[4] = r.y;
+        } else {
+            c[3] = c[4] = 0;
+        }
         c[5] = pln[tile * 64 + lane];
     }
 };
 
 // Byte offset of the down matrix inside a VQ expert.
-__host__ __device__ __forceinline__ size_t vq_down_offset(size_t H, size_t I) {
+__host__ __device__ __forceinline__ size_t vq_down_offset(size_t H, size_t I, bool res) {
     const size_t nv0 = 2 * I * H / 8;
-    return nv0 * 3 / 2 + nv0 / 8 + nv0 + 2 * (2 * I);
+    return nv0 * 3 / 2 + nv0 / 8 + (res ? nv0 : 0) + 2 * (2 * I);
+}
+
+// Bytes of the layer's books in front of the experts.
+template <bool RES>
+__host__ __device__ constexpr size_t vq_books_bytes() {
+    return RES ? kVqBooksBytes : kVq13BooksBytes;
 }
 
 // Compute units of the current device (persistent grids), 256 if unknown.

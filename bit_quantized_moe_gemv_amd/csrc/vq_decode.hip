@@ -65,28 +65,33 @@ struct VdDnLds {
 // same bytes).  (An LDS-direct copy would leave the compiler unable to count
 // the vector loads behind it, so every later wait would be for all loads in
 // flight.)
-constexpr int kBookPieces = kVqEntries + kVqResEntries;  // 16-byte pieces
-constexpr int kBookLoads = (kBookPieces + kVdThreads - 65) / (kVdThreads - 64);  // 15 waves
+template <bool RES>
+constexpr int book_pieces() {  // 16-byte pieces: Cb, then Rb with the residual stage
+    return RES ? kVqEntries + kVqResEntries : kVqEntries;
+}
+constexpr int kBookLoads = (kVqEntries + kVqResEntries + kVdThreads - 65) / (kVdThreads - 64);
 
-template <int NT>
+template <int NT, bool RES>
 __device__ __forceinline__ void load_books(const uint8_t *packed, int t, uint4 (&bv)[kBookLoads]) {
-    static_assert(NT * kBookLoads >= kBookPieces, "book split");
+    constexpr int P = book_pieces<RES>();
+    static_assert(NT * kBookLoads >= P, "book split");
     const uint4 *src = reinterpret_cast<const uint4 *>(packed);
 #pragma unroll
-    for (int j = 0; j < kBookLoads; ++j) bv[j] = src[min(t + NT * j, kBookPieces - 1)];
+    for (int j = 0; j < kBookLoads; ++j) bv[j] = src[min(t + NT * j, P - 1)];
 }
 
-template <int NT>
+template <int NT, bool RES>
 __device__ __forceinline__ void store_books(VdBooks &bk, int t, const uint4 (&bv)[kBookLoads]) {
+    constexpr int P = book_pieces<RES>();
     uint4 *dst = reinterpret_cast<uint4 *>(&bk);
 #pragma unroll
-    for (int j = 0; j < kBookLoads; ++j) dst[min(t + NT * j, kBookPieces - 1)] = bv[j];
+    for (int j = 0; j < kBookLoads; ++j) dst[min(t + NT * j, P - 1)] = bv[j];
 }
 
 // One K step (vector S of the lane's runs) for G groups against the
 // activation piece b: two fp32 dot products per group, Cb[i13] . b and
 // Rb[i8] . b, each over the eight fp16 pairs with exact products.
-template <int S, int G>
+template <int S, int G, bool RES>
 __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBooks &bk, uint4 b,
                                          float (&acc)[G][2]) {
     uint4 cbv[G], rbv[G];
@@ -95,19 +100,22 @@ __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBoo
         uint32_t i13, i8;
         vq_indices<S>(cr[g], i13, i8);
         cbv[g] = bk.cb[i13];
-        rbv[g] = bk.rb[i8];
+        if (RES) rbv[g] = bk.rb[i8];
     }
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         const uint32_t cw[4] = {cbv[g].x, cbv[g].y, cbv[g].z, cbv[g].w};
-        const uint32_t rw[4] = {rbv[g].x, rbv[g].y, rbv[g].z, rbv[g].w};
+        const uint32_t rw[4] = {RES ? rbv[g].x : 0u, RES ? rbv[g].y : 0u, RES ? rbv[g].z : 0u,
+                                RES ? rbv[g].w : 0u};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             acc[g][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, cw[w]),
                                                __builtin_bit_cast(f16x2, bw[w]), acc[g][0], false);
-            acc[g][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, rw[w]),
-                                               __builtin_bit_cast(f16x2, bw[w]), acc[g][1], false);
+            if (RES)
+                acc[g][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, rw[w]),
+                                                   __builtin_bit_cast(f16x2, bw[w]), acc[g][1],
+                                                   false);
         }
     }
     // The sums leave every step through an empty asm: left free, the compiler
@@ -117,17 +125,17 @@ __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBoo
     for (int g = 0; g < G; ++g) asm volatile("" : "+v"(acc[g][0]), "+v"(acc[g][1]));
 }
 
-template <int G>
+template <int G, bool RES>
 __device__ __forceinline__ void vd_tile(const uint32_t (&cr)[G][6], const VdBooks &bk,
                                         const uint4 *bpieces, int q, float (&acc)[G][2]) {
-    vd_kstep<0, G>(cr, bk, bpieces[0 * 4 + q], acc);
-    vd_kstep<1, G>(cr, bk, bpieces[1 * 4 + q], acc);
-    vd_kstep<2, G>(cr, bk, bpieces[2 * 4 + q], acc);
-    vd_kstep<3, G>(cr, bk, bpieces[3 * 4 + q], acc);
-    vd_kstep<4, G>(cr, bk, bpieces[4 * 4 + q], acc);
-    vd_kstep<5, G>(cr, bk, bpieces[5 * 4 + q], acc);
-    vd_kstep<6, G>(cr, bk, bpieces[6 * 4 + q], acc);
-    vd_kstep<7, G>(cr, bk, bpieces[7 * 4 + q], acc);
+    vd_kstep<0, G, RES>(cr, bk, bpieces[0 * 4 + q], acc);
+    vd_kstep<1, G, RES>(cr, bk, bpieces[1 * 4 + q], acc);
+    vd_kstep<2, G, RES>(cr, bk, bpieces[2 * 4 + q], acc);
+    vd_kstep<3, G, RES>(cr, bk, bpieces[3 * 4 + q], acc);
+    vd_kstep<4, G, RES>(cr, bk, bpieces[4 * 4 + q], acc);
+    vd_kstep<5, G, RES>(cr, bk, bpieces[5 * 4 + q], acc);
+    vd_kstep<6, G, RES>(cr, bk, bpieces[6 * 4 + q], acc);
+    vd_kstep<7, G, RES>(cr, bk, bpieces[7 * 4 + q], acc);
 }
 
 // A row's dot product from its four lanes (n, q = 0..3): every lane of row n
@@ -151,7 +159,7 @@ __device__ __forceinline__ int piece_elem(int c) {
 // NSL slices of TJ tiles cover H / 256.  With fewer than kVdWaves such pairs
 // the spare waves repeat the last one's loads and discard the result.
 // ---------------------------------------------------------------------------
-template <int GW, int TJ, int NSL>
+template <int GW, int TJ, int NSL, bool RES>
 __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes, int H,
     int I, int E, int K, const float *__restrict__ logits, int32_t *__restrict__ idx_out,
@@ -192,8 +200,8 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
                                  offsets);
     } else {
         uint4 bv[kBookLoads];
-        load_books<kVdThreads - 64>(packed, tid - 64, bv);
-        store_books<kVdThreads - 64>(lds.bk, tid - 64, bv);
+        load_books<kVdThreads - 64, RES>(packed, tid - 64, bv);
+        store_books<kVdThreads - 64, RES>(lds.bk, tid - 64, bv);
     }
     uint32_t mb = 0;  // largest |x| bits of the thread's 8 values
     {
@@ -209,7 +217,8 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(lds.expert);
 
-    const VqMatrix m(packed + kVqBooksBytes + (size_t)e * expert_bytes, (size_t)2 * I, (size_t)H);
+    const VqMatrix<RES> m(packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes, (size_t)2 * I,
+                          (size_t)H);
     uint32_t cr[TJ][GW][6];
 #pragma unroll
     for (int u = 0; u < TJ; ++u)
@@ -247,7 +256,8 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
 #pragma unroll
     for (int g = 0; g < GW; ++g) acc[g][0] = acc[g][1] = 0.f;
 #pragma unroll
-    for (int u = 0; u < TJ; ++u) vd_tile<GW>(cr[u], lds.bk, &lds.x16[32 * (js * TJ + u)], q, acc);
+    for (int u = 0; u < TJ; ++u)
+        vd_tile<GW, RES>(cr[u], lds.bk, &lds.x16[32 * (js * TJ + u)], q, acc);
 
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
 // (then the upper quarters repeat the last tiles' loads and contribute
 // nothing); routes past k likewise.
 // ---------------------------------------------------------------------------
-template <int TJ>
+template <int TJ, bool RES>
 __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K,
     const int32_t *__restrict__ active, const int32_t *__restrict__ perm,
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
 
     if (tid < 8) lds.rmax[tid] = 0;
     uint4 bv[kBookLoads];
-    load_books<kVdThreads>(packed, tid, bv);
+    load_books<kVdThreads, RES>(packed, tid, bv);
     int ex[2];
     float wgt[2];
 #pragma unroll
@@ -311,19 +321,19 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     for (int k = 0; k < 4; ++k)
         hv[k] = reinterpret_cast<const float4 *>(h + (size_t)min(4 * hh + k, K - 1) * I)[cg];
 
-    const size_t dn_off = vq_down_offset((size_t)H, (size_t)I);
+    const size_t dn_off = vq_down_offset((size_t)H, (size_t)I, RES);
     uint32_t cr[2][TJ][1][6];
     uint32_t gn[2];  // gain of row 16rg + n
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        const VqMatrix m(packed + kVqBooksBytes + (size_t)ex[f] * expert_bytes + dn_off,
-                         (size_t)H, (size_t)I);
+        const VqMatrix<RES> m(packed + vq_books_bytes<RES>() + (size_t)ex[f] * expert_bytes + dn_off,
+                              (size_t)H, (size_t)I);
 #pragma unroll
         for (int u = 0; u < TJ; ++u) m.load((size_t)rg * NJD + j0 + u, lane, cr[f][u][0]);
         gn[f] = m.gain[16 * rg + n];
     }
 
-    store_books<kVdThreads>(lds.bk, tid, bv);
+    store_books<kVdThreads, RES>(lds.bk, tid, bv);
     __syncthreads();
     // per-route exponents from the largest |h| (non-negative floats order as
     // their bit patterns)
@@ -360,7 +370,8 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
         __syncthreads();
         float a1[1][2] = {{0.f, 0.f}};
 #pragma unroll
-        for (int u = 0; u < TJ; ++u) vd_tile<1>(cr[f][u], lds.bk, &lds.h16[r4][32 * (j0 + u)], q, a1);
+        for (int u = 0; u < TJ; ++u)
+            vd_tile<1, RES>(cr[f][u], lds.bk, &lds.h16[r4][32 * (j0 + u)], q, a1);
         acc[f] = row_sum(a1[0]);
     }
 
@@ -386,50 +397,60 @@ bool vq_decode_supported(const Shape &s) {
     const int nj = s.H / 256;
     const bool h_ok = nj == 1 || nj == 2 || nj == 4 || nj == 8 || nj == 16;
     const bool i_ok = s.I == 256 || s.I == 512 || s.I == 1024 || s.I == 2048;
-    return s.fmt == MOE_FMT_VQ13R8 && h_ok && i_ok;
+    return (s.fmt == MOE_FMT_VQ13R8 || s.fmt == MOE_FMT_VQ13) && h_ok && i_ok;
 }
 
-template <int GW, int TJ, int NSL>
+template <int GW, int TJ, int NSL, bool RES>
 static hipError_t vd_gateup_launch(const Shape &s, const uint16_t *x, const uint8_t *packed,
                                    const Workspace &ws, hipStream_t st) {
     const int grid = s.K * (s.I / 16) / kVdPairs;
-    vq_dec_gateup<GW, TJ, NSL><<<grid, kVdThreads, 0, st>>>(
+    vq_dec_gateup<GW, TJ, NSL, RES><<<grid, kVdThreads, 0, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.logits, ws.idx, ws.w, ws.counts,
         ws.offsets, ws.active, ws.perm, ws.inv, static_cast<float *>(ws.h),
         s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
 
-hipError_t launch_vq_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
-                                   const Workspace &ws, hipStream_t st) {
-    if (T != 1 || !vq_decode_supported(s)) return hipErrorInvalidValue;
+template <bool RES>
+static hipError_t vd_gateup_res(const Shape &s, const uint16_t *x, const uint8_t *packed,
+                                const Workspace &ws, hipStream_t st) {
     switch (s.H / 256) {
-        case 1: return vd_gateup_launch<1, 1, 1>(s, x, packed, ws, st);
-        case 2: return vd_gateup_launch<1, 1, 2>(s, x, packed, ws, st);
-        case 4: return vd_gateup_launch<2, 1, 4>(s, x, packed, ws, st);
-        case 8: return vd_gateup_launch<4, 1, 8>(s, x, packed, ws, st);
-        default: return vd_gateup_launch<4, 2, 8>(s, x, packed, ws, st);
+        case 1: return vd_gateup_launch<1, 1, 1, RES>(s, x, packed, ws, st);
+        case 2: return vd_gateup_launch<1, 1, 2, RES>(s, x, packed, ws, st);
+        case 4: return vd_gateup_launch<2, 1, 4, RES>(s, x, packed, ws, st);
+        case 8: return vd_gateup_launch<4, 1, 8, RES>(s, x, packed, ws, st);
+        default: return vd_gateup_launch<4, 2, 8, RES>(s, x, packed, ws, st);
     }
 }
 
-template <int TJ>
+hipError_t launch_vq_decode_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
+                                   const Workspace &ws, hipStream_t st) {
+    if (T != 1 || !vq_decode_supported(s)) return hipErrorInvalidValue;
+    return s.fmt == MOE_FMT_VQ13R8 ? vd_gateup_res<true>(s, x, packed, ws, st)
+                                   : vd_gateup_res<false>(s, x, packed, ws, st);
+}
+
+template <int TJ, bool RES>
 static hipError_t vd_down_launch(const Shape &s, const uint8_t *packed, const Workspace &ws,
                                  float *out, hipStream_t st) {
-    vq_dec_down<TJ><<<s.H / 16, kVdThreads, 0, st>>>(packed, s.expert_bytes, s.H, s.I, s.K,
-                                                     ws.active, ws.perm, ws.w,
-                                                     static_cast<const float *>(ws.h), out);
+    vq_dec_down<TJ, RES><<<s.H / 16, kVdThreads, 0, st>>>(packed, s.expert_bytes, s.H, s.I, s.K,
+                                                          ws.active, ws.perm, ws.w,
+                                                          static_cast<const float *>(ws.h), out);
     return hipGetLastError();
+}
+
+template <bool RES>
+static hipError_t vd_down_res(const Shape &s, const uint8_t *packed, const Workspace &ws,
+                              float *out, hipStream_t st) {
+    return s.I / 256 <= 4 ? vd_down_launch<1, RES>(s, packed, ws, out, st)
+                          : vd_down_launch<2, RES>(s, packed, ws, out, st);
 }
 
 hipError_t launch_vq_decode_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                                  float *out, hipStream_t st) {
     if (T != 1 || !vq_decode_supported(s)) return hipErrorInvalidValue;
-    switch (s.I / 256) {
-        case 1:
-        case 2:
-        case 4: return vd_down_launch<1>(s, packed, ws, out, st);
-        default: return vd_down_launch<2>(s, packed, ws, out, st);
-    }
+    return s.fmt == MOE_FMT_VQ13R8 ? vd_down_res<true>(s, packed, ws, out, st)
+                                   : vd_down_res<false>(s, packed, ws, out, st);
 }
 
 }  // namespace bqmoe

@@ -1,4 +1,6 @@
-// vq_prefill.hip -- large-batch expert kernels for VQ13R8 experts on gfx950.
+// vq_prefill.hip -- large-batch expert kernels for VQ13R8 and VQ13 experts on
+// gfx950 (VQ13 layers have no residual stage: the A operand is Cb itself, and
+// everything below that concerns Rb drops out).
 //
 // A VQ13R8 weight is w[n][8v+d] = gain[n] * (Cb[i13][d] + Rb[i8][d]): an
 // 8-wide codeword from a per-layer book of 8192 entries (13-bit index: a
@@ -41,7 +43,6 @@ constexpr int kVqThreads = kVqWaves * 64;
 constexpr int kVqGroups = 4;  // row groups (16 rows) per wave; 512 rows per block item
 constexpr int kVqRing = 3;    // B sub-stages in LDS
 constexpr int kVqChunkLanes = 2;  // an expert's 64-token chunks are dealt to 2 items
-constexpr int kVqCodeLoads = 3 * kVqGroups;  // loads per wave per super-step
 
 struct VqLds {
     uint4 cb[kVqEntries];     // 128 KiB
@@ -131,37 +132,43 @@ __global__ __launch_bounds__(256) void vq_hpack_kernel(const float *__restrict__
     if (threadIdx.x == 0) hexp[blockIdx.x] = s;
 }
 
-// A operand of K step S for one row group: Cb[i13] + Rb[i8] in fp16.
-// c[0..2] code12, c[3..4] res, c[5] plane byte.
-template <int S>
+// Book rows of K step S for one row group: Cb[i13] and (with the residual
+// stage) Rb[i8].  c[0..2] code12, c[3..4] res, c[5] plane byte.
+template <int S, bool RES>
 __device__ __forceinline__ void gather_a(const uint32_t (&c)[6], const VqLds &lds, uint4 &cbv,
                                          uint4 &rbv) {
     uint32_t i13, i8;
     vq_indices<S>(c, i13, i8);
     cbv = lds.cb[i13];
-    rbv = lds.rb[i8];
+    if (RES) rbv = lds.rb[i8];
+}
+
+// The A operand: Cb + Rb rounded once to fp16, or Cb alone.
+template <bool RES>
+__device__ __forceinline__ f16x8 a_operand(uint4 cbv, uint4 rbv) {
+    return RES ? add_f16x8(cbv, rbv) : __builtin_bit_cast(f16x8, cbv);
 }
 
 // One sub-step (two K steps) of a wave: 2 x 4 groups x NTT token tiles MFMAs.
-template <int U, int NTT>
+template <int U, int NTT, bool RES>
 __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], const VqLds &lds,
                                            int slot, int lane, f32x4 (&acc)[kVqGroups][NTT]) {
     const int q = lane >> 4, n = lane & 15;
     uint4 cb0[kVqGroups], rb0[kVqGroups], cb1[kVqGroups], rb1[kVqGroups];
     uint4 b0[NTT], b1[NTT];
 #pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U>(cr[g], lds, cb0[g], rb0[g]);
+    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U, RES>(cr[g], lds, cb0[g], rb0[g]);
 #pragma unroll
     for (int t = 0; t < NTT; ++t)
         b0[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][0][q][16 * t + n]);
 #pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U + 1>(cr[g], lds, cb1[g], rb1[g]);
+    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U + 1, RES>(cr[g], lds, cb1[g], rb1[g]);
 #pragma unroll
     for (int t = 0; t < NTT; ++t)
         b1[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][1][q][16 * t + n]);
     f16x8 a0[kVqGroups];
 #pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) a0[g] = add_f16x8(cb0[g], rb0[g]);
+    for (int g = 0; g < kVqGroups; ++g) a0[g] = a_operand<RES>(cb0[g], rb0[g]);
 #pragma unroll
     for (int t = 0; t < NTT; ++t)
 #pragma unroll
@@ -170,7 +177,7 @@ __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], c
                 a0[g], __builtin_bit_cast(f16x8, b0[t]), acc[g][t], 0, 0, 0);
     f16x8 a1[kVqGroups];
 #pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) a1[g] = add_f16x8(cb1[g], rb1[g]);
+    for (int g = 0; g < kVqGroups; ++g) a1[g] = a_operand<RES>(cb1[g], rb1[g]);
 #pragma unroll
     for (int t = 0; t < NTT; ++t)
 #pragma unroll
@@ -189,9 +196,10 @@ __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], c
 // NTT = 4: 64-token chunks over all E experts.  NTT = 1 (batches of at most
 // 16 tokens, so at most 16 routes per expert): one 16-token chunk per item,
 // and the items run over the active experts only (the list the small-batch
-// routing writes), so no MFMA works on absent tokens or experts.
+// routing writes), so no MFMA works on absent tokens or experts.  RES: the
+// layer has the residual stage (VQ13R8) or not (VQ13).
 // ---------------------------------------------------------------------------
-template <int MODE, int NTT>
+template <int MODE, int NTT, bool RES>
 __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int E,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
@@ -208,7 +216,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     {  // both books -> LDS, once per block
         const uint4 *books = reinterpret_cast<const uint4 *>(packed);
         for (int i = tid; i < kVqEntries; i += kVqThreads) lds.cb[i] = books[i];
-        for (int i = tid; i < kVqResEntries; i += kVqThreads) lds.rb[i] = books[kVqEntries + i];
+        if (RES)
+            for (int i = tid; i < kVqResEntries; i += kVqThreads) lds.rb[i] = books[kVqEntries + i];
     }
     __syncthreads();
 
@@ -219,11 +228,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const int nslice = MODE == 0 ? I / 256 : (H + 511) / 512;
     const int per_e = nslice * kLanes;
     const size_t nvec = (size_t)NROW * NK / 8;
-    size_t mat_off = 0;
-    if (MODE == 1) {
-        const size_t nv0 = (size_t)2 * I * H / 8;
-        mat_off = nv0 * 3 / 2 + nv0 / 8 + nv0 + (size_t)2 * (2 * I);
-    }
+    const size_t mat_off = MODE == 1 ? vq_down_offset((size_t)H, (size_t)I, RES) : 0;
+    constexpr int kCodeLoads = (RES ? 3 : 2) * kVqGroups;  // loads per wave per super-step
 
     // blockIdx -> items: with E and the grid multiples of 8, the blocks of one
     // XCD (the dispatcher deals blocks round-robin over the 8 XCDs) take the
@@ -240,11 +246,11 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
         const int slice = rest / kLanes, chl = rest % kLanes;
         const int p0 = offsets[e];
         const int ne = offsets[e + 1] - p0;
-        const uint8_t *mat = packed + kVqBooksBytes + (size_t)e * expert_bytes + mat_off;
+        const uint8_t *mat = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
         const uint8_t *c12 = mat;
         const uint8_t *pln = c12 + nvec * 3 / 2;
         const uint8_t *res = pln + nvec / 8;
-        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + nvec);
+        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
 
         int grp[kVqGroups];
 #pragma unroll
@@ -273,7 +279,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                 for (int g = 0; g < kVqGroups; ++g) {
                     const size_t tile = (size_t)grp[g] * NJ + J;
                     const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
-                    const uint2 r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
+                    uint2 r = make_uint2(0u, 0u);
+                    if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
                     const uint32_t p = pln[tile * 64 + lane];
                     cr[slot][g][0] = c.x;
                     cr[slot][g][1] = c.y;
@@ -318,7 +325,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                     for (int u = 0; u < 4; ++u) {
                         const int S = 4 * J + u;
                         if (u == 1)
-                            vq_wait_vmcnt<kVqCodeLoads>();
+                            vq_wait_vmcnt<kCodeLoads>();
                         else
                             vq_wait_vmcnt<0>();
                         store_b(min(S + 1, lastS));
@@ -327,10 +334,10 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                         if (u == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
                         if (J < NJ) {
                             const int slot = S % kVqRing;
-                            if (u == 0) vq_substep<0, NTT>(cr[jj], lds, slot, lane, acc);
-                            if (u == 1) vq_substep<1, NTT>(cr[jj], lds, slot, lane, acc);
-                            if (u == 2) vq_substep<2, NTT>(cr[jj], lds, slot, lane, acc);
-                            if (u == 3) vq_substep<3, NTT>(cr[jj], lds, slot, lane, acc);
+                            if (u == 0) vq_substep<0, NTT, RES>(cr[jj], lds, slot, lane, acc);
+                            if (u == 1) vq_substep<1, NTT, RES>(cr[jj], lds, slot, lane, acc);
+                            if (u == 2) vq_substep<2, NTT, RES>(cr[jj], lds, slot, lane, acc);
+                            if (u == 3) vq_substep<3, NTT, RES>(cr[jj], lds, slot, lane, acc);
                         }
                     }
                 }
@@ -391,12 +398,21 @@ static int vq_grid(int items) {
     return max(g, 1);
 }
 
+template <int MODE, int NTT, bool RES>
+static void vq_launch3(const Shape &s, int items, const uint8_t *packed, const Workspace &ws,
+                       const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
+    vq_prefill_kernel<MODE, NTT, RES><<<vq_grid(items), kVqThreads, 0, st>>>(
+        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.active, bsrc, bexp,
+        out);
+}
+
 template <int MODE, int NTT>
 static void vq_launch(const Shape &s, int items, const uint8_t *packed, const Workspace &ws,
                       const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
-    vq_prefill_kernel<MODE, NTT><<<vq_grid(items), kVqThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.active, bsrc, bexp,
-        out);
+    if (s.fmt == MOE_FMT_VQ13R8)
+        vq_launch3<MODE, NTT, true>(s, items, packed, ws, bsrc, bexp, out, st);
+    else
+        vq_launch3<MODE, NTT, false>(s, items, packed, ws, bsrc, bexp, out, st);
 }
 
 // Batches of at most kDecodeMaxTokens tokens (routed by the small-batch

@@ -67,25 +67,34 @@ enum {
  *   of the index), res one byte per vector; gains are one fp16 per row.
  *   Weight w[n][8v+d] = gain[n] * (Cb[i13][d] + Rb[i8][d]); every sum
  *   Cb[i][d] + Rb[j][d] must be finite in fp16 (|sum| <= 65504).
+ *
+ * MOE_FMT_VQ13 (the 13-bit stage alone -- Baekpica VQ card, "Recipe": every
+ * layer carries it, 32 layers add the residual stage, and the 13-bit stage is
+ * byte-identical with and without it): packed = [Cb: 8192 x 8 fp16] then
+ * n_experts experts of 3*inter*hidden*13/64 + 2*(2*inter + hidden) bytes:
+ *   [gu code12][gu plane][gu gain][dn code12][dn plane][dn gain],
+ * each region as in MOE_FMT_VQ13R8; weight w[n][8v+d] = gain[n] * Cb[i13][d].
  */
-enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2 };
+enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2, MOE_FMT_VQ13 = 3 };
 
 /* Path selection: AUTO uses the weight-streaming decode kernels for batches of
- * at most MOE_DECODE_MAX_TOKENS tokens (MXFP4) or of one token (VQ13R8) and
- * the grouped-GEMM prefill kernels above that; DECODE and PREFILL force one of
- * them (DECODE with a larger T returns MOE_EINVAL).  The decode kernels exist
- * for MXFP4 layers with hidden/256 and inter powers of two (inter <= 2048) and
- * for VQ13R8 layers with hidden/256 a power of two up to 16 and inter one of
- * 256, 512, 1024, 2048: other layers run the grouped-GEMM kernels at every
- * batch size, and forcing DECODE on them returns MOE_EUNSUPPORTED.
+ * at most MOE_DECODE_MAX_TOKENS tokens (MXFP4) or of one token (VQ13R8,
+ * VQ13) and the grouped-GEMM prefill kernels above that; DECODE and PREFILL
+ * force one of them (DECODE with a larger T returns MOE_EINVAL).  The decode
+ * kernels exist for MXFP4 layers with hidden/256 and inter powers of two
+ * (inter <= 2048) and for VQ layers with hidden/256 a power of two up to 16
+ * and inter one of 256, 512, 1024, 2048: other layers run the grouped-GEMM
+ * kernels at every batch size, and forcing DECODE on them returns
+ * MOE_EUNSUPPORTED.
  *
  * Numerics of the grouped-GEMM kernels: MXFP4 weights are exact in bf16 and
  * the intermediate h enters the down projection as an exact bf16 pair
  * (hi + lo); VQ13R8 weights enter as fp16(Cb + Rb) (one rounding, relative
- * error <= 2^-11) with the row gain applied in fp32, and x and h as fp16 rows
- * scaled by an exact power of two per row (relative error <= 2^-11 for h);
- * the VQ13R8 decode kernels use the same operands.  All products accumulate
- * in fp32. */
+ * error <= 2^-11; VQ13 weights enter as Cb exactly) with the row gain
+ * applied in fp32, and x and h as fp16 rows scaled by an exact power of two
+ * per row (relative error <= 2^-11 for h).  The VQ decode kernels take Cb and
+ * Rb unrounded and the activations as above.  All products accumulate in
+ * fp32. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 #define MOE_DECODE_MAX_TOKENS 16
 
@@ -100,7 +109,7 @@ enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_SIGMOID = 1 };
 
 typedef struct {
     int32_t hidden;     /* H: multiple of 256 */
-    int32_t inter;      /* I: multiple of 128 (MXFP4) or 256 (VQ13R8) */
+    int32_t inter;      /* I: multiple of 128 (MXFP4) or 256 (VQ13R8, VQ13) */
     int32_t n_experts;  /* E: 1..256 */
     int32_t top_k;      /* k: 1..8 and k <= E */
     int32_t max_tokens; /* largest T a forward call may pass: 1..65536 */

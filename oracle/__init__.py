@@ -20,6 +20,7 @@ SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 FMT_MXFP4 = 1
 FMT_VQ13R8 = 2
+FMT_VQ13 = 3
 
 
 def build(force: bool = True) -> str:

@@ -50,6 +50,7 @@
 
 #define OR_FMT_MXFP4 1
 #define OR_FMT_VQ13R8 2
+#define OR_FMT_VQ13 3
 #define OR_VQ_ENTRIES 8192
 #define OR_VQ_RES_ENTRIES 256
 
@@ -132,7 +133,8 @@ double oracle_mxfp4_weight(const uint8_t *codes, const uint8_t *scales,
  * (n/16)*(K/256) + k/256, 512 vectors each.  Vector (tile row r, vector column
  * j = (k%256)/8) sits at stream position ((j/8)*16 + r)*8 + j%8 of its tile.
  * code12 is a little-endian 12-bit stream, plane a little-endian bit stream
- * (the plane bit is bit 12 of the index), res one byte per vector. */
+ * (the plane bit is bit 12 of the index), res one byte per vector.  A layer
+ * of the 13-bit stage alone (res and rb both NULL) has w = gain * Cb[i13]. */
 double oracle_vq_weight(const uint8_t *code12, const uint8_t *plane,
                         const uint8_t *res, const uint16_t *gain,
                         const uint16_t *cb, const uint16_t *rb,
@@ -146,8 +148,9 @@ double oracle_vq_weight(const uint8_t *code12, const uint8_t *plane,
     int i12 = (int)((two >> (bit % 8)) & 0xFFF);
     int p = (plane[pos / 8] >> (pos % 8)) & 1;
     int i13 = i12 | (p << 12);
-    int i8 = res[pos];
     double c = oracle_fp16(cb[(int64_t)i13 * 8 + d]);
+    if (res == NULL) return oracle_fp16(gain[n]) * c;
+    int i8 = res[pos];
     double rr = oracle_fp16(rb[(int64_t)i8 * 8 + d]);
     return oracle_fp16(gain[n]) * (c + rr);
 }
@@ -164,13 +167,14 @@ static int64_t mx_expert_bytes(int64_t H, int64_t I) {
     return 2 * I * H / 2 + 2 * I * H / 32 + H * I / 2 + H * I / 32;
 }
 
-static int64_t vq_matrix_bytes(int64_t N, int64_t K) {
+/* with_res: the matrix has the residual index region (VQ13R8) or not (VQ13) */
+static int64_t vq_matrix_bytes(int64_t N, int64_t K, int with_res) {
     int64_t nvec = N * K / 8;
-    return nvec * 3 / 2 + nvec / 8 + nvec + N * 2;
+    return nvec * 3 / 2 + nvec / 8 + (with_res ? nvec : 0) + N * 2;
 }
 
-static int64_t vq_expert_bytes(int64_t H, int64_t I) {
-    return vq_matrix_bytes(2 * I, H) + vq_matrix_bytes(H, I);
+static int64_t vq_expert_bytes(int64_t H, int64_t I, int with_res) {
+    return vq_matrix_bytes(2 * I, H, with_res) + vq_matrix_bytes(H, I, with_res);
 }
 
 /* Weight of expert e, matrix m (0 = gate/up [2I x H], 1 = down [H x I]). */
@@ -187,16 +191,19 @@ static double layer_weight(const layer_t *L, int64_t e, int m, int64_t n, int64_
         return m == 0 ? oracle_mxfp4_weight(gc, gs, N, K, n, k)
                       : oracle_mxfp4_weight(dc, ds, N, K, n, k);
     } else {
+        /* VQ13R8: [Cb][Rb] then experts with a res region; VQ13: [Cb] then
+         * experts without one */
+        const int with_res = L->fmt == OR_FMT_VQ13R8;
         const uint16_t *cb = (const uint16_t *)L->packed;
-        const uint16_t *rb = cb + OR_VQ_ENTRIES * 8;
-        const uint8_t *base = L->packed + (OR_VQ_ENTRIES + OR_VQ_RES_ENTRIES) * 8 * 2
-                              + e * vq_expert_bytes(H, I);
-        if (m == 1) base += vq_matrix_bytes(2 * I, H);
+        const uint16_t *rb = with_res ? cb + OR_VQ_ENTRIES * 8 : NULL;
+        const int64_t books = (OR_VQ_ENTRIES + (with_res ? OR_VQ_RES_ENTRIES : 0)) * 8 * 2;
+        const uint8_t *base = L->packed + books + e * vq_expert_bytes(H, I, with_res);
+        if (m == 1) base += vq_matrix_bytes(2 * I, H, with_res);
         int64_t nvec = N * K / 8;
         const uint8_t *c12 = base;
         const uint8_t *pl = c12 + nvec * 3 / 2;
-        const uint8_t *rs = pl + nvec / 8;
-        const uint16_t *gn = (const uint16_t *)(rs + nvec);
+        const uint8_t *rs = with_res ? pl + nvec / 8 : NULL;
+        const uint16_t *gn = (const uint16_t *)(pl + nvec / 8 + (with_res ? nvec : 0));
         return oracle_vq_weight(c12, pl, rs, gn, cb, rb, N, K, n, k);
     }
 }
@@ -389,9 +396,9 @@ int oracle_moe_forward(int fmt, int64_t H, int64_t I, int64_t E, int64_t k, int 
                        const uint8_t *packed, const uint16_t *x, const float *wr, int64_t T,
                        const int64_t *tokens, int64_t n, double *out, int32_t *idx, double *w,
                        float *logits) {
-    if (fmt != OR_FMT_MXFP4 && fmt != OR_FMT_VQ13R8) return -1;
+    if (fmt != OR_FMT_MXFP4 && fmt != OR_FMT_VQ13R8 && fmt != OR_FMT_VQ13) return -1;
     if (H % 256 != 0 || I % 32 != 0 || k < 1 || k > E) return -1;
-    if (fmt == OR_FMT_VQ13R8 && (I % 256 != 0 || E < 1)) return -1;
+    if (fmt != OR_FMT_MXFP4 && (I % 256 != 0 || E < 1)) return -1;
     layer_t L = {fmt, H, I, E, packed};
     if (tokens == NULL) n = T;
     double *xd = malloc(sizeof(double) * (size_t)H);

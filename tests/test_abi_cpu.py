@@ -150,3 +150,17 @@ def test_routing_field_validated(lib):
         with pytest.raises(bq.MoeError) as ei:
             bq.workspace_size(256, 128, 8, 2, 16, routing=r)
         assert ei.value.status == bq.MOE_EINVAL
+
+
+def test_vq13_descriptor_sizes(lib):
+    import workloads as W
+    for h, i, e in ((256, 256, 8), (4096, 2048, 256), (768, 512, 4)):
+        assert bq.packed_size(h, i, e, 2, fmt=bq.MOE_FMT_VQ13) == W.packed_bytes(W.FMT_VQ13, h, i, e)
+    with pytest.raises(bq.MoeError) as ei:
+        bq.packed_size(256, 128, 8, 2, fmt=bq.MOE_FMT_VQ13)
+    assert ei.value.status == bq.MOE_EINVAL
+    # batch-1 decode kernels cover VQ13 like VQ13R8
+    bq.workspace_size(4096, 2048, 256, 8, 1, bq.MOE_FMT_VQ13, bq.MOE_PATH_DECODE)
+    with pytest.raises(bq.MoeError) as ei:
+        bq.packed_size(256, 256, 8, 2, fmt=4)
+    assert ei.value.status == bq.MOE_EINVAL

@@ -162,6 +162,42 @@ def test_vq_zero_residual_equals_r13_only(oracle_lib):
     assert np.array_equal(got, want)
 
 
+def test_vq13_layer_is_the_13_bit_stage(oracle_lib):
+    """A VQ13 layer (no residual stage) holding the 13-bit stage of a VQ13R8
+    layer whose residual book is zero decodes to the same weights and gives
+    the same layer output bit for bit (the 13-bit stage is byte-identical
+    with and without the residual stage: Baekpica VQ card, "Recipe").  The
+    VQ13 buffer is the VQ13R8 one with the residual regions cut out."""
+    rng = np.random.default_rng(4)
+    cb = rng.standard_normal((8192, 8)).astype(np.float16)
+    rb = np.zeros((256, 8), dtype=np.float16)
+    h, i, e = 256, 256, 2
+    packed = _vq_layer_with(lambda r, n, k: r.integers(0, 8192, size=(n, k // 8)),
+                            lambda r, n, k: r.integers(0, 256, size=(n, k // 8)),
+                            cb, rb, lambda r, n: r.uniform(0.5, 1.5, n).astype(np.float16),
+                            h=h, i=i, e=e)
+    p13 = W.vq13_from_vq13r8(packed, h, i, e)
+    assert p13.size == W.packed_bytes(W.FMT_VQ13, h, i, e)
+    for ex in range(e):
+        for which in (0, 1):
+            a = oracle_lib.decode_matrix(W.FMT_VQ13R8, h, i, e, packed, ex, which)
+            b = oracle_lib.decode_matrix(W.FMT_VQ13, h, i, e, p13, ex, which)
+            assert np.array_equal(a, b)
+    wl = W.TINY_VQ13.replace(experts=e, tokens=5)
+    x, wr = W.make_x(wl), W.make_router(wl)
+    ra = oracle_lib.moe_forward(W.FMT_VQ13R8, h, i, e, 2, packed, x, wr)
+    rb13 = oracle_lib.moe_forward(W.FMT_VQ13, h, i, e, 2, p13, x, wr)
+    assert np.array_equal(ra["out"], rb13["out"])
+
+
+def test_vq13_sizes():
+    """13 bits per 8 weights plus an fp16 gain per row: 5,128,192 bytes per
+    MiMo-shaped expert; the layer's book is the 128 KiB Cb alone."""
+    assert W.vq_expert_bytes(4096, 2048, res=False) == 3 * 2048 * 4096 * 13 // 64 + 2 * (
+        2 * 2048 + 4096) == 5128192
+    assert W.packed_bytes(W.FMT_VQ13, 4096, 2048, 256) == 8192 * 16 + 256 * 5128192
+
+
 def test_vq_unit_vector_books_closed_form(oracle_lib):
     """Cb[j] = ((j % 1024) + 1) * 2^-(j // 1024) * e_(j mod 8) and
     Rb[m] = -m/256 * e_((m+3) mod 8), all exact in fp16.  Then

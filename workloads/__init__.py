@@ -49,11 +49,14 @@ import numpy as np
 
 FMT_MXFP4 = 1
 FMT_VQ13R8 = 2
+FMT_VQ13 = 3
+VQ_FORMATS = (FMT_VQ13R8, FMT_VQ13)
 
 VQ_BOOK_ENTRIES = 8192
 VQ_RES_ENTRIES = 256
 VQ_DIM = 8
 VQ_BOOKS_BYTES = (VQ_BOOK_ENTRIES + VQ_RES_ENTRIES) * VQ_DIM * 2
+VQ13_BOOKS_BYTES = VQ_BOOK_ENTRIES * VQ_DIM * 2
 
 
 # ---------------------------------------------------------------------------
@@ -80,24 +83,25 @@ def mxfp4_expert_bytes(h: int, i: int) -> int:
     return mxfp4_expert_regions(h, i)["dn_scales"][1]
 
 
-def vq_matrix_regions(n: int, k: int) -> tuple[int, int, int, int]:
-    """(code12, plane, res, gain) byte counts of one VQ matrix."""
+def vq_matrix_regions(n: int, k: int, res: bool = True) -> tuple[int, int, int, int]:
+    """(code12, plane, res, gain) byte counts of one VQ matrix (res 0 for VQ13)."""
     nvec = n * k // VQ_DIM
-    return nvec * 3 // 2, nvec // 8, nvec, n * 2
+    return nvec * 3 // 2, nvec // 8, nvec if res else 0, n * 2
 
 
-def vq_expert_regions(h: int, i: int) -> dict[str, tuple[int, int]]:
+def vq_expert_regions(h: int, i: int, res: bool = True) -> dict[str, tuple[int, int]]:
     out, off = {}, 0
     for prefix, (n, k) in (("gu", (2 * i, h)), ("dn", (h, i))):
-        c, p, r, g = vq_matrix_regions(n, k)
+        c, p, r, g = vq_matrix_regions(n, k, res)
         for name, size in (("code12", c), ("plane", p), ("res", r), ("gain", g)):
-            out[f"{prefix}_{name}"] = (off, off + size)
+            if size:
+                out[f"{prefix}_{name}"] = (off, off + size)
             off += size
     return out
 
 
-def vq_expert_bytes(h: int, i: int) -> int:
-    return vq_expert_regions(h, i)["dn_gain"][1]
+def vq_expert_bytes(h: int, i: int, res: bool = True) -> int:
+    return vq_expert_regions(h, i, res)["dn_gain"][1]
 
 
 def packed_bytes(fmt: int, h: int, i: int, e: int) -> int:
@@ -105,7 +109,19 @@ def packed_bytes(fmt: int, h: int, i: int, e: int) -> int:
         return e * mxfp4_expert_bytes(h, i)
     if fmt == FMT_VQ13R8:
         return VQ_BOOKS_BYTES + e * vq_expert_bytes(h, i)
+    if fmt == FMT_VQ13:
+        return VQ13_BOOKS_BYTES + e * vq_expert_bytes(h, i, res=False)
     raise ValueError(f"unknown format {fmt}")
+
+
+def vq13_from_vq13r8(packed: np.ndarray, h: int, i: int, e: int) -> np.ndarray:
+    """The VQ13 buffer holding the same 13-bit stage as a VQ13R8 buffer: the
+    residual book and the residual index regions dropped, every other byte
+    kept in order (byte slicing only)."""
+    full = vq_expert_regions(h, i, True)
+    ex = packed[VQ_BOOKS_BYTES:].reshape(e, vq_expert_bytes(h, i, True))
+    keep = [ex[:, a:b] for name, (a, b) in full.items() if not name.endswith("_res")]
+    return np.concatenate([packed[:VQ13_BOOKS_BYTES], np.concatenate(keep, axis=1).reshape(-1)])
 
 
 # ---------------------------------------------------------------------------
@@ -164,8 +180,13 @@ VQ_PREFILL = Workload("mimo_vq_prefill_t2048", tokens=2048, hidden=4096, inter=2
 # Test-only tiny VQ layer (VQ tiles need multiples of 256 in both widths).
 TINY_VQ = Workload("tiny_vq", tokens=16, hidden=256, inter=256, experts=8, top_k=2,
                    fmt=FMT_VQ13R8, seed=6)
+# the 13-bit stage alone (every VQ layer has it; 32 of 48 add the residual)
+TINY_VQ13 = TINY_VQ.replace(name="tiny_vq13", fmt=FMT_VQ13, seed=7)
+VQ13_DECODE = Workload("mimo_vq13_decode_t1", tokens=1, hidden=4096, inter=2048, experts=256,
+                       top_k=8, fmt=FMT_VQ13, seed=8)
 
-PRESETS = {w.name: w for w in (TINY, DECODE, VERIFY, PREFILL, VQ_PREFILL, TINY_VQ)}
+PRESETS = {w.name: w for w in (TINY, DECODE, VERIFY, PREFILL, VQ_PREFILL, TINY_VQ, TINY_VQ13,
+                               VQ13_DECODE)}
 
 # stream numbers inside SeedSequence(seed).spawn(N_STREAMS)
 _S_X, _S_ROUTER, _S_CODES, _S_SCALES, _S_HOT, _S_SCALED, _S_BOOKS, _S_GAINS = range(8)
@@ -235,7 +256,7 @@ def make_experts(w: Workload) -> np.ndarray:
     """The packed expert buffer (uint8) of the workload's format."""
     if w.fmt == FMT_MXFP4:
         return _make_mxfp4(w)
-    if w.fmt == FMT_VQ13R8:
+    if w.fmt in VQ_FORMATS:
         return _make_vq(w)
     raise ValueError(w.fmt)
 
@@ -254,13 +275,14 @@ def _make_mxfp4(w: Workload) -> np.ndarray:
 
 
 def _make_vq(w: Workload) -> np.ndarray:
+    res = w.fmt == FMT_VQ13R8
     rs = _streams(w.seed)
-    books = rs[_S_BOOKS].standard_normal(
-        ((VQ_BOOK_ENTRIES + VQ_RES_ENTRIES) * VQ_DIM,), dtype=np.float32).astype(np.float16)
-    s = vq_expert_bytes(w.hidden, w.inter)
+    entries = VQ_BOOK_ENTRIES + (VQ_RES_ENTRIES if res else 0)
+    books = rs[_S_BOOKS].standard_normal((entries * VQ_DIM,), dtype=np.float32).astype(np.float16)
+    s = vq_expert_bytes(w.hidden, w.inter, res)
     # Uniform bytes give uniform 12-bit codes, plane bits and residual indices.
     ex = rs[_S_CODES].integers(0, 256, size=(w.experts, s), dtype=np.uint8)
-    reg = vq_expert_regions(w.hidden, w.inter)
+    reg = vq_expert_regions(w.hidden, w.inter, res)
     for name, k in (("gu_gain", w.hidden), ("dn_gain", w.inter)):
         a, b = reg[name]
         rows = (b - a) // 2
