@@ -142,7 +142,8 @@ class Bench:
             torch.cuda.synchronize()
         return self._vq13
 
-    def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0):
+    def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0,
+            path=0):
         torch, bq, W = self.torch, self.bq, self.W
         T = tokens_per_step
         n_batches = steps + warmup
@@ -155,7 +156,8 @@ class Bench:
             xs.append(torch.from_numpy(x.view("int16")).to("cuda").view(torch.bfloat16))
         xall = torch.cat(xs).view(n_batches, T, wl.hidden)
         wr = torch.from_numpy(W.make_router(wl)).to("cuda")
-        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt)
+        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt, path,
+                            routing=wl.routing)
         out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
         st = self.stream.cuda_stream
         _, base, stride, L = self.layers if layers is None else layers
@@ -353,6 +355,20 @@ def main():
         vqv = b.run(W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed"), 100, 10,
                     16, layers=b.vq_layers(), replay=20)
         extra["vq_verify_t16"] = vqv
+        log("verify-width sweep")
+        sweep = {}
+        for t in (1, 3, 4, 8, 16):
+            wl = W.VERIFY.replace(tokens=t, name=f"mimo_verify_t{t}_skewed")
+            row = {}
+            for name, pth in (("decode", bq.MOE_PATH_DECODE), ("grouped", bq.MOE_PATH_PREFILL)):
+                r = b.run(wl, 100, 10, t, profile=False, path=pth)
+                row[name + "_us"] = round(r["ms_per_step"] * 1e3, 2)
+            vq = b.run(W.VERIFY.replace(tokens=t, fmt=W.FMT_VQ13R8), 50, 5, t, profile=False,
+                       layers=b.vq_layers())
+            row["vq13r8_auto_us"] = round(vq["ms_per_step"] * 1e3, 2)
+            row["distinct_experts"] = vq["distinct_experts_last_step"]
+            sweep[f"t{t}"] = row
+        extra["verify_width_sweep"] = sweep
         log("VQ13 decode T=1")
         extra["vq13_decode_t1"] = b.run(W.VQ13_DECODE, 200, 20, 1, layers=b.vq13_layers(),
                                         replay=100)
