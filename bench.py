@@ -281,7 +281,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode only")
-    ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "copy"],
+    ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "vq_decode",
+                                       "copy"],
                     default=None,
                     help="run one workload without the report (for profilers)")
     ap.add_argument("--no-peaks", action="store_true")
@@ -316,7 +317,8 @@ def main():
 
     if args.only:
         wl = {"decode": W.DECODE, "verify": W.VERIFY, "prefill": W.PREFILL,
-              "vq_prefill": W.VQ_PREFILL}[args.only]
+              "vq_prefill": W.VQ_PREFILL,
+              "vq_decode": W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1")}[args.only]
         res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False,
                     layers=b.vq_layers() if wl.fmt == W_FMT_VQ else None)
         log(json.dumps(res))
