@@ -360,10 +360,10 @@ def main():
         log("verify-width sweep")
         sweep = {}
         for t in (1, 3, 4, 8, 16):
-            wl = W.VERIFY.replace(tokens=t, name=f"mimo_verify_t{t}_skewed")
+            wv = W.VERIFY.replace(tokens=t, name=f"mimo_verify_t{t}_skewed")
             row = {}
             for name, pth in (("decode", bq.MOE_PATH_DECODE), ("grouped", bq.MOE_PATH_PREFILL)):
-                r = b.run(wl, 100, 10, t, profile=False, path=pth)
+                r = b.run(wv, 100, 10, t, profile=False, path=pth)
                 row[name + "_us"] = round(r["ms_per_step"] * 1e3, 2)
             vq = b.run(W.VERIFY.replace(tokens=t, fmt=W.FMT_VQ13R8), 50, 5, t, profile=False,
                        layers=b.vq_layers())
