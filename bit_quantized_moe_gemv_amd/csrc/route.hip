@@ -110,16 +110,40 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// block-wide exclusive scan of one int per thread (blockDim = 256 or 1024)
+// ---------------------------------------------------------------------------
+__device__ int block_exclusive_scan(int v, int *total, int *lds /* >= 16 ints */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int incl = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) lds[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int q = 0; q < nw; ++q) {
+        const int c = lds[q];
+        if (q < wave) base += c;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------
 // Small batches (T <= 16): router logits, then the whole routing in one block.
 //
 // router_small_kernel: each wave computes one expert's logits for up to TT
 // tokens, with every load (MAXG 256-column groups of W and x) issued before the
 // first FMA, in the same summation order as router_kernel.
 //
-// route_small_kernel (one block of 16 waves): top-k + softmax, one wave per
-// token; counts (a count does not depend on order); the active list (ballot
-// prefix over experts); and a stable grouping in which route r takes its rank
-// among earlier routes of the same expert.  A separate launch costs less than
+// route_small_kernel (one block of 16 waves): top-k and weights, one wave per
+// token; a 16-bit mask per expert of the tokens routed to it (LDS atomic or);
+// counts as mask popcounts, offsets and the active list as block scans; and
+// the stable grouping, in which route r of token t takes position
+// offsets[e] + popcount(mask[e] below bit t).  A separate launch costs less than
 // publishing the logits across the XCDs from inside the router kernel (a
 // device-scope release per block plus an arrival counter).
 // ---------------------------------------------------------------------------
@@ -131,9 +155,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     bool sigmoid) {
     __shared__ int s_idx[kDecodeMaxTokens * kMaxTopK];
-    __shared__ int s_wtot[kRouteThreads / 64];
+    __shared__ uint32_t s_mask[kMaxExperts];  // bit t: token t routes to the expert
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_scan[kRouteThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int R = T * K;
+    if (tid < kMaxExperts) s_mask[tid] = 0;
     for (int t = wave; t < T; t += nw) {
         int idx[kMaxTopK];
         float w[kMaxTopK];
@@ -149,44 +176,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
             s_idx[t * K + lane] = iv;
         }
     }
-    lds_barrier();
-    // expert e: its count and offset are direct counts over the <= 128 routes
+    __syncthreads();
+    // which tokens route to each expert (a token's k experts are distinct)
+    if (tid < R) atomicOr(&s_mask[s_idx[tid]], 1u << (tid / K));
+    __syncthreads();
+    // counts, and offsets as their exclusive scan; the active list in
+    // ascending expert order (threads of the first four waves hold experts)
     const int e = tid;
-    int cnt = 0, below = 0;
-    if (e < E)
-        for (int r = 0; r < R; ++r) {
-            const int x = s_idx[r];
-            cnt += (x == e);
-            below += (x < e);
-        }
-    const bool act = e < E && cnt > 0;
-    const uint64_t mask = __ballot(act);
-    if (lane == 0) s_wtot[wave] = __popcll(mask);
-    // route r: its position is the number of routes ordered before it by
-    // (expert, route id) -- a stable grouping
-    for (int r = tid; r < R; r += blockDim.x) {
-        const int er = s_idx[r];
-        int pos = 0;
-        for (int r2 = 0; r2 < R; ++r2) {
-            const int x = s_idx[r2];
-            pos += (x < er) || (x == er && r2 < r);
-        }
-        perm[pos] = r;
-        inv[r] = pos;
-    }
-    lds_barrier();
+    const int cnt = e < E ? __popc(s_mask[e]) : 0;
+    int total;
+    const int off = block_exclusive_scan(cnt, &total, s_scan);
+    int n_act;
+    const int apos = block_exclusive_scan(cnt > 0 ? 1 : 0, &n_act, s_scan);
     if (e < E) {
+        s_off[e] = off;
         counts[e] = cnt;
-        offsets[e] = below;
-        if (e == E - 1) offsets[E] = R;
+        offsets[e] = off;
+        if (cnt > 0) active[1 + apos] = e;
     }
-    int base = 0, tot = 0;
-    for (int q = 0; q < nw; ++q) {
-        base += (q < wave) ? s_wtot[q] : 0;
-        tot += s_wtot[q];
+    if (tid == 0) {
+        offsets[E] = total;
+        active[0] = n_act;
     }
-    if (act) active[1 + base + __popcll(mask & ((1ull << lane) - 1ull))] = e;
-    if (tid == 0) active[0] = tot;
+    __syncthreads();
+    // route r = t*K + s goes to position offsets[e] + (number of earlier tokens
+    // routed to e): the stable grouping by (expert, token)
+    if (tid < R) {
+        const int er = s_idx[tid], t = tid / K;
+        const int pos = s_off[er] + __popc(s_mask[er] & ((1u << t) - 1u));
+        perm[pos] = tid;
+        inv[tid] = pos;
+    }
 }
 
 template <int TT, int MAXG>
@@ -287,29 +307,6 @@ hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t s
     topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(ws.logits, T, s.E, s.K, ws.idx, ws.w,
                                              s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// block-wide exclusive scan of one int per thread (blockDim = 256 or 1024)
-// ---------------------------------------------------------------------------
-__device__ int block_exclusive_scan(int v, int *total, int *lds /* >= 16 ints */) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int incl = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-    }
-    if (lane == 63) lds[wave] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
-    for (int q = 0; q < nw; ++q) {
-        const int c = lds[q];
-        if (q < wave) base += c;
-        tot += c;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
 }
 
 // ---------------------------------------------------------------------------
