@@ -342,7 +342,7 @@ def main():
 
     if not args.no_extra:
         log("verify T=16 (skewed routing)")
-        ver = b.run(W.VERIFY, max(200, args.steps // 4), 50, 16)
+        ver = b.run(W.VERIFY, max(200, args.steps // 4), 50, 16, replay=50)
         a = algorithmic(W.VERIFY, ver["distinct_experts_last_step"], 16)
         extra["verify_t16"] = {**ver, "step_algorithmic_bytes": a["step_bytes"],
                                "step_hbm_gbs": round(a["step_bytes"] / (ver["ms_per_step"] * 1e-3) / 1e9, 1)}

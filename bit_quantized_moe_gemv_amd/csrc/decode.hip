@@ -18,6 +18,7 @@
 namespace bqmoe {
 
 constexpr int kDecTC = 4;  // routes (tokens) per pass through the staged operand
+constexpr int kDecRS = 4;  // row groups a gate/up block streams one after another
 
 // bf16 pairs of a 16-byte fp4 block: out[b] = columns (2b, 2b+1) * scale.
 __device__ __forceinline__ void fp4x32_to_bf16(const uint4 v, float scale, bf16x2 *out) {
@@ -76,7 +77,7 @@ __device__ __forceinline__ void reg_fence(uint4 &v) {
 // kernel), every block takes the slot-th selected expert in ascending order,
 // and block (0, 0) publishes the routing for the down kernel and
 // moe_layer_routing.  This replaces a separate routing launch.
-template <int NJ, int TC, bool R1>
+template <int NJ, int TC, bool R1, int RS>
 __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
     int H, int I, int E, int K, int32_t *__restrict__ active, int32_t *__restrict__ offsets,
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     int32_t *__restrict__ idx_out, float *__restrict__ w_out, int32_t *__restrict__ counts,
     int32_t *__restrict__ inv, bool sigmoid) {
     extern __shared__ __align__(16) uint16_t xs[];  // [TC][H]
-    __shared__ float red[4][TC][16];
+    __shared__ float red[RS][4][TC][64];  // [row group][wave][token][lane]: lanes 0..15 used
     const int slot = blockIdx.x;
     int e, p0, ne;
     if (R1) {
@@ -114,13 +115,13 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
         p0 = offsets[e];
         ne = offsets[e + 1] - p0;
     }
-    const int rg = blockIdx.y;
+    const int rg0 = blockIdx.y * RS;  // first of the block's RS row groups
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, q = lane >> 4;
     const int mat = wave >> 1, kh = wave & 1;
 
     const size_t kt = (size_t)(H / 32);  // tiles along K per row group
-    const size_t grp = (size_t)(mat ? I / 16 + rg : rg);
+    const size_t grp = (size_t)(mat ? I / 16 + rg0 : rg0);
     const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const uint8_t *cbase = ex + (grp * kt + (size_t)kh * NJ * 4) * 256;          // wave's first tile
     const uint8_t *sbase = ex + (size_t)I * H + (grp * kt + (size_t)kh * NJ * 4) * 16;
@@ -148,12 +149,17 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
             xv[i] = reinterpret_cast<const uint4 *>(x + (size_t)t * H)[c];
         }
         __builtin_amdgcn_sched_barrier(0);  // x loads first, then the weight ring
+        // The wave's stream: RS row groups one after another, NJ super-steps
+        // each; row group r starts r*rstride bytes (r*sstride scale bytes)
+        // further on.  The ring runs across row-group boundaries.
+        constexpr int JJ = RS * NJ;
+        const uint32_t rstride = (uint32_t)(kt * 256), sstride = (uint32_t)(kt * 16);
         uint4 ring[kRing];
         uint32_t sring[kRing];
 #pragma unroll
-        for (int j = 0; j < kRing && j < NJ; ++j) {
-            ring[j] = ld16(cbase, coff + j * 1024);
-            sring[j] = sbase[soff + j * 64];
+        for (int j = 0; j < kRing && j < JJ; ++j) {
+            ring[j] = ld16(cbase, (j / NJ) * rstride + coff + (j % NJ) * 1024);
+            sring[j] = sbase[(j / NJ) * sstride + soff + (j % NJ) * 64];
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -163,20 +169,25 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
 
         float acc[TC];
 #pragma unroll
-        for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
+        for (int jj = 0; jj < JJ; ++jj) {
+            const int r = jj / NJ, j = jj % NJ;
+            if (j == 0) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            uint4 wv = ring[j % kRing];
-            uint32_t sv = sring[j % kRing];
+                for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
+            }
+            uint4 wv = ring[jj % kRing];
+            uint32_t sv = sring[jj % kRing];
             reg_fence(wv);
             reg_fence(sv);
             const float sc = e8m0_to_f32(sv);
-            if (j + kRing < NJ) {
-                uint32_t o = coff + (j + kRing) * 1024, so = soff + (j + kRing) * 64;
+            if (jj + kRing < JJ) {
+                const int jn = jj + kRing;
+                uint32_t o = (jn / NJ) * rstride + coff + (jn % NJ) * 1024;
+                uint32_t so = (jn / NJ) * sstride + soff + (jn % NJ) * 64;
                 reg_fence(o);
                 reg_fence(so);
-                ring[j % kRing] = ld16(cbase, o);
-                sring[j % kRing] = sbase[so];
+                ring[jj % kRing] = ld16(cbase, o);
+                sring[jj % kRing] = sbase[so];
             }
             bf16x2 w2[16];
             fp4x32_to_bf16(wv, sc, w2);
@@ -196,19 +207,24 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
+            if (j == NJ - 1) {  // row group r done: the wave's partial sums to LDS
 #pragma unroll
-        for (int tt = 0; tt < TC; ++tt) {
-            acc[tt] += __shfl_xor(acc[tt], 16, 64);
-            acc[tt] += __shfl_xor(acc[tt], 32, 64);
-            if (q == 0) red[wave][tt][n] = acc[tt];
+                for (int tt = 0; tt < TC; ++tt) {
+                    acc[tt] += __shfl_xor(acc[tt], 16, 64);
+                    acc[tt] += __shfl_xor(acc[tt], 32, 64);
+                    red[r][wave][tt][lane] = acc[tt];  // every lane: no branch in the stream
+                }
+            }
         }
+        // one barrier after the whole stream (a barrier or a global store
+        // inside it would make the compiler drain the weight ring), then
+        // SwiGLU and h for the block's RS row groups
         lds_barrier();
-        if (tid < nt * 16) {
-            const int tt = tid >> 4, nn = tid & 15;
-            const float g = red[0][tt][nn] + red[1][tt][nn];
-            const float u = red[2][tt][nn] + red[3][tt][nn];
-            h[(size_t)(p0 + c0 + tt) * I + 16 * rg + nn] = silu_f32(g) * u;
+        for (int i = tid; i < RS * nt * 16; i += 256) {
+            const int r = i / (nt * 16), tt = (i >> 4) % nt, nn = i & 15;
+            const float g = red[r][0][tt][nn] + red[r][1][tt][nn];
+            const float u = red[r][2][tt][nn] + red[r][3][tt][nn];
+            h[(size_t)(p0 + c0 + tt) * I + 16 * (rg0 + r) + nn] = silu_f32(g) * u;
         }
     }
 }
@@ -339,12 +355,12 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
     }
 }
 
-template <int NJ, int TC, bool R1>
+template <int NJ, int TC, bool R1, int RS>
 static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
     const int slots = min(s.E, T * s.K);
-    dim3 grid(slots, s.I / 16);
-    decode_gateup_mxfp4<NJ, TC, R1><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
+    dim3 grid(slots, s.I / (16 * RS));
+    decode_gateup_mxfp4<NJ, TC, R1, RS><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.active, ws.offsets, ws.perm,
         static_cast<float *>(ws.h), ws.logits, ws.idx, ws.w, ws.counts, ws.inv,
         s.routing == MOE_ROUTE_SIGMOID);
@@ -354,8 +370,9 @@ static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const 
 template <int NJ>
 static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
                                    const uint8_t *packed, const Workspace &ws, hipStream_t st) {
-    return T == 1 ? gateup_launch<NJ, 1, true>(s, T, x, packed, ws, st)
-                  : gateup_launch<NJ, kDecTC, false>(s, T, x, packed, ws, st);
+    constexpr int RS = NJ >= 32 ? 1 : kDecRS;  // (the unrolled stream grows with RS * NJ)
+    return T == 1 ? gateup_launch<NJ, 1, true, RS>(s, T, x, packed, ws, st)
+                  : gateup_launch<NJ, kDecTC, false, RS>(s, T, x, packed, ws, st);
 }
 
 bool decode_supported(const Shape &s) {
