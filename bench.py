@@ -286,6 +286,8 @@ def main():
                     default=None,
                     help="run one workload without the report (for profilers)")
     ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--replay", type=int, default=0,
+                    help="with --only: also time each stage alone over this many launches")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -320,7 +322,7 @@ def main():
               "vq_prefill": W.VQ_PREFILL,
               "vq_decode": W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1")}[args.only]
         res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False,
-                    layers=b.vq_layers() if wl.fmt == W_FMT_VQ else None)
+                    layers=b.vq_layers() if wl.fmt == W_FMT_VQ else None, replay=args.replay)
         log(json.dumps(res))
         return
 

@@ -61,11 +61,11 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256(R * 4);                   // inv
     b += align256(R * s.I * 4);             // h
     b += align256(R * s.H * 4);             // y
+    b += align256(R * s.I * 2);             // h16
+    b += align256(R * 4);                   // hexp
     if (is_vq_format(s.fmt)) {
         b += align256((size_t)tmax * s.H * 2);  // x16
         b += align256((size_t)tmax * 4);        // xexp
-        b += align256(R * s.I * 2);             // h16
-        b += align256(R * 4);                   // hexp
     }
     return b;
 }
@@ -88,15 +88,13 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
     ws->h = take(R * s.I * 4);
     ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
+    ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
+    ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));
     ws->x16 = nullptr;
     ws->xexp = nullptr;
-    ws->h16 = nullptr;
-    ws->hexp = nullptr;
     if (is_vq_format(s.fmt)) {
         ws->x16 = reinterpret_cast<uint16_t *>(take((size_t)tmax * s.H * 2));
         ws->xexp = reinterpret_cast<int32_t *>(take((size_t)tmax * 4));
-        ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
-        ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));
     }
 }
 

@@ -47,9 +47,10 @@ struct Workspace {
     int32_t *active;   // [1 + E]: n_active, then active experts ascending
     int32_t *perm;     // [Rmax]
     int32_t *inv;      // [Rmax]
-    void *h;           // [Rmax][I]: fp32 (decode, VQ prefill) or two bf16 arrays (MXFP4 prefill)
+    void *h;           // [Rmax][I] fp32
     float *y;          // [Rmax][H] fp32 per-route expert outputs
-    // VQ prefill only (null otherwise): fp16 rows with a power-of-two exponent each
+    // fp16 rows with a power-of-two exponent each: h16/hexp feed the down GEMM
+    // of both formats, x16/xexp (VQ only, null otherwise) the VQ gate/up GEMM
     uint16_t *x16;     // [Tmax][H]
     int32_t *xexp;     // [Tmax]
     uint16_t *h16;     // [Rmax][I]
@@ -84,6 +85,8 @@ hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const
                                  const Workspace &ws, hipStream_t st);
 hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                                hipStream_t st);
+// h (fp32, R rows) -> h16 and hexp
+hipError_t launch_hpack(const Shape &s, int R, const Workspace &ws, hipStream_t st);
 hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
                                     const uint8_t *packed, const Workspace &ws, hipStream_t st);
 hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,

@@ -29,12 +29,21 @@
 // 128J+32q .. +31; K step s uses bytes 4s..4s+3 (columns 128J+32q+8s..+7),
 // and the B operand of lane (m, q) at step s is x[m][128J+32q+8s..+7].
 //
-// SwiGLU is fused into the gate/up epilogue in fp32.  Expert intermediates
-// exceed fp16's range (TrevorJS card, "Recipe"; benthecarman EXL3 card,
-// "Bitrate") and a single bf16 is too coarse for the down projection, so h is
-// stored as hi = bf16(h), lo = bf16(h - hi) and the down GEMM runs both
-// halves through the MFMA into the same fp32 accumulators.
+// SwiGLU is fused into the gate/up epilogue in fp32, and h is written in
+// fp32.  Expert intermediates exceed fp16's range (TrevorJS card, "Recipe";
+// benthecarman EXL3 card, "Bitrate") and a single bf16 is too coarse for the
+// down projection, so a packing pass stores each h row as fp16 times a power
+// of two of its own (h16 = h * 2^-s_r, 11 significant bits), and the down GEMM
+// runs on the fp16 matrix cores (v_mfma_f32_16x16x32_f16): one pass, where a
+// bf16 hi + lo split of h would take two.  Its A operand is the weight times
+// 2^(e - b_g), e the block's E8M0 exponent and b_g the largest exponent of the
+// 16-row group, which is exact in fp16 while a group's exponents span at most
+// 13 (further below b_g the products only lose bits that sit 2^-14 under the
+// group's largest weights); the epilogue multiplies by 2^(b_g - 127 + s_r).
+#include <type_traits>
+
 #include "moe_internal.h"
+#include "vq_common.h"
 
 namespace bqmoe {
 
@@ -75,8 +84,27 @@ __device__ __forceinline__ void map_expert_block(int bid, int E, int NB, int *e,
     }
 }
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_op(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Four packed fp4 bytes -> eight fp16, each times `scale` (byte b: columns 2b, 2b+1).
+__device__ __forceinline__ f16x8 fp4x8_to_f16x8(uint32_t v, float scale) {
+    union { f16x8 v8; f16x2 v2[4]; } r;
+    r.v2[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 0);
+    r.v2[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 1);
+    r.v2[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 2);
+    r.v2[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, 3);
+    return r.v8;
+}
+
+// 2^(e - b) for an E8M0 exponent e at most b, 0 below 2^-126.
+__device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
+    const int d = (int)e + 127 - b;
+    return d > 0 ? __uint_as_float((uint32_t)d << 23) : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -112,20 +140,25 @@ struct GuLds {
 // next K step's B operands and dequantised A operands are prepared before the
 // current K step's MFMAs (double buffering).  Every step dequantises, even
 // with no token tile, so no load is left in flight on a ring register.
+// F16: fp16 operands, the weights scaled relative to the group exponents b[g].
+template <bool F16>
 __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const GuLds &lds,
                                         int slot, int wave, int mt, int lane,
-                                        f32x4 (&acc)[kGuGroups][4]) {
+                                        const int (&b)[kGuGroups], f32x4 (&acc)[kGuGroups][4]) {
+    using V8 = std::conditional_t<F16, f16x8, bf16x8>;
     const int q = lane >> 4, n = lane & 15;
     float scale[kGuGroups];
 #pragma unroll
-    for (int g = 0; g < kGuGroups; ++g)
-        scale[g] = e8m0_to_f32(lds.sc[slot][wave][0][64 * g + 16 * q + n]);
-    bf16x8 a[2][kGuGroups];
-    bf16x8 bv[2][4];
+    for (int g = 0; g < kGuGroups; ++g) {
+        const uint32_t e = lds.sc[slot][wave][0][64 * g + 16 * q + n];
+        scale[g] = F16 ? e8m0_rel_f32(e, b[g]) : e8m0_to_f32(e);
+    }
+    V8 a[2][kGuGroups];
+    V8 bv[2][4];
     auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            bv[buf][t] = *reinterpret_cast<const bf16x8 *>(
+            bv[buf][t] = *reinterpret_cast<const V8 *>(
                 &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
     };
     auto dequant = [&](int buf, int ks) {
@@ -133,7 +166,10 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
         for (int g = 0; g < kGuGroups; ++g) {
             const uint4 c = code[g];
             const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
-            a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
+            if constexpr (F16)
+                a[buf][g] = fp4x8_to_f16x8(d, scale[g]);
+            else
+                a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
         }
     };
     load_b(0, 0);
@@ -150,15 +186,21 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
             if (t < mt) {
 #pragma unroll
                 for (int g = 0; g < kGuGroups; ++g)
-                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][t], acc[g][t]);
+                    acc[g][t] = mfma_op(a[cur][g], bv[cur][t], acc[g][t]);
             }
     }
 }
 
+__device__ __forceinline__ uint32_t byte_max(uint32_t w) {
+    return max(max(w & 0xFFu, (w >> 8) & 0xFFu), max((w >> 16) & 0xFFu, w >> 24));
+}
+
+template <bool F16>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
                                             int nsuper, const int (&grp)[kGuGroups], int sgrp,
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
-                                            int mt, f32x4 (&acc)[kGuGroups][4]) {
+                                            int mt, f32x4 (&acc)[kGuGroups][4],
+                                            int (&b)[kGuGroups]) {
     constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
     uint4 ring[kGuRing][kGuGroups];
     uint32_t goff[kGuGroups];
@@ -181,6 +223,31 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
     const int last = nsuper - 1;
 #pragma unroll
     for (int j = 0; j < kGuRing - 1; ++j) issue(j, min(j, last));
+    if constexpr (F16) {
+        // b[g] = the largest E8M0 exponent of row group grp[g] (kt tiles of 16
+        // bytes), read while the first steps are in flight
+        // (the four groups' loads of a pass are issued together; past the
+        // last tile lanes repeat it)
+        uint32_t m[kGuGroups] = {0, 0, 0, 0};
+        for (size_t c0 = 0; c0 < kt; c0 += 64) {
+            const size_t c = min(c0 + (size_t)lane, kt - 1);
+            uint4 v[kGuGroups];
+#pragma unroll
+            for (int g = 0; g < kGuGroups; ++g)
+                v[g] = *reinterpret_cast<const uint4 *>(scales + ((size_t)grp[g] * kt + c) * 16);
+#pragma unroll
+            for (int g = 0; g < kGuGroups; ++g)
+                m[g] = max(m[g], max(max(byte_max(v[g].x), byte_max(v[g].y)),
+                                     max(byte_max(v[g].z), byte_max(v[g].w))));
+        }
+#pragma unroll
+        for (int g = 0; g < kGuGroups; ++g) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                m[g] = max(m[g], (uint32_t)__shfl_xor((int)m[g], o, 64));
+            b[g] = __builtin_amdgcn_readfirstlane((int)m[g]);
+        }
+    }
     for (int J0 = 0; J0 < nsuper; J0 += kGuRing) {
 #pragma unroll
         for (int jj = 0; jj < kGuRing; ++jj) {
@@ -188,7 +255,7 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
             wait_vmcnt<(kGuRing - 2) * C>();  // step J has landed
             stage_barrier();
             issue((jj + kGuRing - 1) % kGuRing, min(J + kGuRing - 1, last));
-            if (J < nsuper) gu_step(ring[jj], lds, jj, wave, mt, lane, acc);
+            if (J < nsuper) gu_step<F16>(ring[jj], lds, jj, wave, mt, lane, b, acc);
         }
     }
     wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
@@ -197,7 +264,7 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
 __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
     int H, int I, int K, int E, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ perm, uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo) {
+    const int32_t *__restrict__ perm, float *__restrict__ h) {
     __shared__ __align__(16) GuLds lds;
     int e, part;
     map_expert_block(blockIdx.x, E, (I / 128) * 2, &e, &part);
@@ -230,8 +297,9 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 64 * th) stage_barrier();  // previous chunk's readers are done with the rings
-        gu_pipeline(ex, ex + (size_t)I * H, kt, H / 128, grp, sgrp, lds, brow, wave, lane, mt,
-                    acc);
+        int unused[kGuGroups];
+        gu_pipeline<false>(ex, ex + (size_t)I * H, kt, H / 128, grp, sgrp, lds, brow, wave, lane,
+                           mt, acc, unused);
         // epilogue: lane holds rows 4q..4q+3 of each group for token 16t + n;
         // gate group i pairs with up group 2 + i
 #pragma unroll
@@ -242,18 +310,12 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int gg = 8 * b + 2 * wave + i;  // gate group
-                    uint32_t hi[4], lo[4];
+                    float hv[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float hv = silu_f32(acc[i][t][jj]) * acc[2 + i][t][jj];
-                        hi[jj] = f32_to_bf16_rne(hv);
-                        lo[jj] = f32_to_bf16_rne(hv - bf16_to_f32(hi[jj]));
-                    }
-                    const size_t col = (size_t)16 * gg + 4 * q;
-                    *reinterpret_cast<uint2 *>(h_hi + p * I + col) =
-                        make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-                    *reinterpret_cast<uint2 *>(h_lo + p * I + col) =
-                        make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                    for (int jj = 0; jj < 4; ++jj)
+                        hv[jj] = silu_f32(acc[i][t][jj]) * acc[2 + i][t][jj];
+                    *reinterpret_cast<float4 *>(h + p * I + (size_t)16 * gg + 4 * q) =
+                        make_float4(hv[0], hv[1], hv[2], hv[3]);
                 }
             }
         }
@@ -262,114 +324,16 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
 
 // ---------------------------------------------------------------------------
 // down.  Grid: E * H/256 * 2 blocks of 4 waves, two blocks per CU as in
-// gate/up.  Block (b, half th) owns output row groups 16b..16b+15 (wave w:
-// 16b+4w..+3) and the expert's tokens in 64-token chunks th, th+2, ...; the h
-// rows are contiguous (route-position order), hi and lo halves run through
-// the MFMA into the same accumulators.  The B stage of a step holds both
-// halves (32 KiB), so the ring is 2 deep: a step's loads are issued one step
-// ahead and waited for at the next step.
+// gate/up, on the same pipeline with fp16 operands.  Block (b, half th) owns
+// output row groups 16b..16b+15 (wave w: 16b+4w..+3) and the expert's tokens
+// in 64-token chunks th, th+2, ...; the h16 rows are contiguous (route-position
+// order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
 // ---------------------------------------------------------------------------
-constexpr int kDnPfWaves = 4;
-constexpr int kDnPfThreads = kDnPfWaves * 64;
-constexpr int kDnPfGroups = 4;
-constexpr int kDnPfRing = 2;
-
-struct DnLds {
-    uint8_t b[kDnPfRing][2][4][64][64];           // [slot][hi, lo][chunk group][token][64 B]
-    uint8_t sc[kDnPfRing][kDnPfWaves][4][256];    // [slot][wave][replica][group, tile, row]
-};
-
-__device__ __forceinline__ void dn_step(const uint4 (&code)[kDnPfGroups], const DnLds &lds,
-                                        int slot, int wave, int mt, int lane,
-                                        f32x4 (&acc)[kDnPfGroups][4]) {
-    const int q = lane >> 4, n = lane & 15;
-    float scale[kDnPfGroups];
-#pragma unroll
-    for (int g = 0; g < kDnPfGroups; ++g)
-        scale[g] = e8m0_to_f32(lds.sc[slot][wave][0][64 * g + 16 * q + n]);
-    bf16x8 a[2][kDnPfGroups];
-    bf16x8 bv[2][2][4];
-    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks, both halves
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                bv[buf][hl][t] = *reinterpret_cast<const bf16x8 *>(
-                    &lds.b[slot][hl][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
-    };
-    auto dequant = [&](int buf, int ks) {
-#pragma unroll
-        for (int g = 0; g < kDnPfGroups; ++g) {
-            const uint4 c = code[g];
-            const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
-            a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
-        }
-    };
-    load_b(0, 0);
-    dequant(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int cur = ks & 1;
-        if (ks < 3) {
-            load_b(cur ^ 1, ks + 1);
-            dequant(cur ^ 1, ks + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (t < mt) {
-#pragma unroll
-                for (int g = 0; g < kDnPfGroups; ++g) {
-                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][0][t], acc[g][t]);
-                    acc[g][t] = mfma_bf16(a[cur][g], bv[cur][1][t], acc[g][t]);
-                }
-            }
-    }
-}
-
-__device__ __forceinline__ void dn_pipeline(const uint8_t *codes, const uint8_t *scales,
-                                            size_t kt, int nsuper, const int (&grp)[kDnPfGroups],
-                                            int sgrp, DnLds &lds, const uint16_t *rhi,
-                                            const uint16_t *rlo, int wave, int lane, int mt,
-                                            f32x4 (&acc)[kDnPfGroups][4]) {
-    constexpr int C = 8 + 1 + kDnPfGroups;  // loads per wave per step
-    static_assert(C < 16, "vmcnt range");
-    uint4 ring[kDnPfRing][kDnPfGroups];
-    uint32_t goff[kDnPfGroups];
-#pragma unroll
-    for (int g = 0; g < kDnPfGroups; ++g)
-        goff[g] = (uint32_t)((size_t)grp[g] * kt * 256) + lane * 16;
-    const int swz = (lane & 3) ^ ((lane >> 4) & 3);
-    auto issue = [&](int slot, int J) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            copy_lds16(rhi + 128 * J + 8 * (4 * i + swz), lds.b[slot][0][i][16 * wave]);
-            copy_lds16(rlo + 128 * J + 8 * (4 * i + swz), lds.b[slot][1][i][16 * wave]);
-        }
-        copy_lds16(scales + ((size_t)sgrp * kt + 4 * J + (lane & 3)) * 16, lds.sc[slot][wave][0]);
-#pragma unroll
-        for (int g = 0; g < kDnPfGroups; ++g)
-            ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
-    };
-    const int last = nsuper - 1;
-    issue(0, 0);
-    for (int J0 = 0; J0 < nsuper; J0 += kDnPfRing) {
-#pragma unroll
-        for (int jj = 0; jj < kDnPfRing; ++jj) {
-            const int J = J0 + jj;
-            wait_vmcnt<(kDnPfRing - 2) * C>();  // step J has landed
-            stage_barrier();
-            issue((jj + kDnPfRing - 1) % kDnPfRing, min(J + kDnPfRing - 1, last));
-            if (J < nsuper) dn_step(ring[jj], lds, jj, wave, mt, lane, acc);
-        }
-    }
-    wait_vmcnt<0>();
-}
-
-__global__ __launch_bounds__(kDnPfThreads, 2) void prefill_down_mxfp4(
+__global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
-    const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h_hi,
-    const uint16_t *__restrict__ h_lo, float *__restrict__ y) {
-    __shared__ __align__(16) DnLds lds;
+    const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h16,
+    const int32_t *__restrict__ hexp, float *__restrict__ y) {
+    __shared__ __align__(16) GuLds lds;
     int e, part;
     map_expert_block(blockIdx.x, E, (H / 256) * 2, &e, &part);
     const int b = part >> 1, th = part & 1;
@@ -381,32 +345,39 @@ __global__ __launch_bounds__(kDnPfThreads, 2) void prefill_down_mxfp4(
     const int n = lane & 15, q = lane >> 4;
     const uint8_t *codes = packed + (size_t)e * expert_bytes + (size_t)I * H + (size_t)I * H / 16;
     const size_t kt = (size_t)(I / 32);
-    int grp[kDnPfGroups];
+    int grp[kGuGroups];
 #pragma unroll
-    for (int g = 0; g < kDnPfGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
+    for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
     const int sgrp = 16 * b + 4 * wave + ((lane >> 2) & 3);
 
     for (int c0 = 64 * th; c0 < ne; c0 += 128) {
         const int nt = min(64, ne - c0);
         const int mt = (nt + 15) / 16;
-        const size_t r = (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
-        f32x4 acc[kDnPfGroups][4];
+        const uint16_t *brow = h16 + (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
+        f32x4 acc[kGuGroups][4];
 #pragma unroll
-        for (int g = 0; g < kDnPfGroups; ++g)
+        for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 64 * th) stage_barrier();
-        dn_pipeline(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, sgrp, lds, h_hi + r,
-                    h_lo + r, wave, lane, mt, acc);
+        int bexp[kGuGroups];
+        gu_pipeline<true>(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, sgrp, lds, brow,
+                          wave, lane, mt, acc, bexp);
+        int hs[4];  // row exponents of the lane's tokens, fetched together
+#pragma unroll
+        for (int t = 0; t < 4; ++t) hs[t] = hexp[p0 + c0 + min(16 * t + n, nt - 1)] - 127;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int m = 16 * t + n;
             if (m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
-                for (int g = 0; g < kDnPfGroups; ++g)
+                for (int g = 0; g < kGuGroups; ++g) {
+                    const int sc = bexp[g] + hs[t];
                     *reinterpret_cast<float4 *>(y + p * H + 16 * grp[g] + 4 * q) =
-                        make_float4(acc[g][t][0], acc[g][t][1], acc[g][t][2], acc[g][t][3]);
+                        make_float4(ldexpf(acc[g][t][0], sc), ldexpf(acc[g][t][1], sc),
+                                    ldexpf(acc[g][t][2], sc), ldexpf(acc[g][t][3], sc));
+                }
             }
         }
     }
@@ -414,19 +385,18 @@ __global__ __launch_bounds__(kDnPfThreads, 2) void prefill_down_mxfp4(
 
 hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                  const Workspace &ws, hipStream_t st) {
-    uint16_t *hh = static_cast<uint16_t *>(ws.h);
-    uint16_t *hl = hh + (size_t)T * s.K * s.I;
     prefill_gateup_mxfp4<<<s.E * (s.I / 128) * 2, kGuThreads, 0, st>>>(
-        x, packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, hh, hl);
+        x, packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm,
+        static_cast<float *>(ws.h));
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                                hipStream_t st) {
-    const uint16_t *hh = static_cast<const uint16_t *>(ws.h);
-    const uint16_t *hl = hh + (size_t)T * s.K * s.I;
-    prefill_down_mxfp4<<<s.E * (s.H / 256) * 2, kDnPfThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, hh, hl, ws.y);
+    hipError_t e = launch_hpack(s, T * s.K, ws, st);
+    if (e != hipSuccess) return e;
+    prefill_down_mxfp4<<<s.E * (s.H / 256) * 2, kGuThreads, 0, st>>>(
+        packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, ws.h16, ws.hexp, ws.y);
     return hipGetLastError();
 }
 

@@ -100,36 +100,57 @@ __global__ __launch_bounds__(256) void vq_xpack_kernel(const uint16_t *__restric
 }
 
 // ---------------------------------------------------------------------------
-// h (fp32) -> fp16 rows scaled by 2^-s_r.  One block per route row.
+// h (fp32) -> fp16 rows scaled by 2^-s_r, the B operand of both formats' down
+// GEMM.  One wave per route row, four rows per block; with NV > 0 the lane
+// keeps its NV float4 (I = 256 * NV) in registers between the maximum and the
+// conversion, otherwise it reads the row twice.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void vq_hpack_kernel(const float *__restrict__ h, int I,
-                                                       uint16_t *__restrict__ h16,
-                                                       int32_t *__restrict__ hexp) {
-    __shared__ uint32_t smax;
-    if (threadIdx.x == 0) smax = 0;
-    __syncthreads();
-    const float *row = h + (size_t)blockIdx.x * I;
+__device__ __forceinline__ uint2 f32x4_to_f16x4(float4 v, int s) {
+    const _Float16 a = (_Float16)ldexpf(v.x, -s), b = (_Float16)ldexpf(v.y, -s);
+    const _Float16 c = (_Float16)ldexpf(v.z, -s), d = (_Float16)ldexpf(v.w, -s);
+    return make_uint2((uint32_t)__builtin_bit_cast(uint16_t, a) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16),
+                      (uint32_t)__builtin_bit_cast(uint16_t, c) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, d) << 16));
+}
+
+__device__ __forceinline__ uint32_t abs_max_bits(float4 v, uint32_t m) {
+    m = max(m, __float_as_uint(v.x) & 0x7FFFFFFFu);
+    m = max(m, __float_as_uint(v.y) & 0x7FFFFFFFu);
+    m = max(m, __float_as_uint(v.z) & 0x7FFFFFFFu);
+    return max(m, __float_as_uint(v.w) & 0x7FFFFFFFu);
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void hpack_kernel(const float *__restrict__ h, int I, int R,
+                                                    uint16_t *__restrict__ h16,
+                                                    int32_t *__restrict__ hexp) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
+    const float4 *row = reinterpret_cast<const float4 *>(h + (size_t)r * I);
+    uint2 *dst = reinterpret_cast<uint2 *>(h16 + (size_t)r * I);
     uint32_t m = 0;
-    for (int i = threadIdx.x * 4; i < I; i += 256 * 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + i);
-        m = max(m, __float_as_uint(v.x) & 0x7FFFFFFFu);
-        m = max(m, __float_as_uint(v.y) & 0x7FFFFFFFu);
-        m = max(m, __float_as_uint(v.z) & 0x7FFFFFFFu);
-        m = max(m, __float_as_uint(v.w) & 0x7FFFFFFFu);
+    if constexpr (NV > 0) {
+        float4 v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = row[64 * i + lane];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) m = abs_max_bits(v[i], m);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        const int s = fp16_row_exponent(m);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) dst[64 * i + lane] = f32x4_to_f16x4(v[i], s);
+        if (lane == 0) hexp[r] = s;
+    } else {
+        for (int i = lane; i < I / 4; i += 64) m = abs_max_bits(row[i], m);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+        const int s = fp16_row_exponent(m);
+        for (int i = lane; i < I / 4; i += 64) dst[i] = f32x4_to_f16x4(row[i], s);
+        if (lane == 0) hexp[r] = s;
     }
-    const int s = fp16_row_exponent(block_max_bits(m, &smax));
-    uint16_t *dst = h16 + (size_t)blockIdx.x * I;
-    for (int i = threadIdx.x * 4; i < I; i += 256 * 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(row + i);
-        const _Float16 a = (_Float16)ldexpf(v.x, -s), b = (_Float16)ldexpf(v.y, -s);
-        const _Float16 c = (_Float16)ldexpf(v.z, -s), d = (_Float16)ldexpf(v.w, -s);
-        *reinterpret_cast<uint2 *>(dst + i) =
-            make_uint2((uint32_t)__builtin_bit_cast(uint16_t, a) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16),
-                       (uint32_t)__builtin_bit_cast(uint16_t, c) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, d) << 16));
-    }
-    if (threadIdx.x == 0) hexp[blockIdx.x] = s;
 }
 
 // Book rows of K step S for one row group: Cb[i13] and (with the residual
@@ -415,6 +436,19 @@ static void vq_launch(const Shape &s, int items, const uint8_t *packed, const Wo
         vq_launch3<MODE, NTT, false>(s, items, packed, ws, bsrc, bexp, out, st);
 }
 
+hipError_t launch_hpack(const Shape &s, int R, const Workspace &ws, hipStream_t st) {
+    const float *h = static_cast<const float *>(ws.h);
+    const int nb = (R + 3) / 4;
+    switch (s.I % 256 ? 0 : s.I / 256) {
+        case 1: hpack_kernel<1><<<nb, 256, 0, st>>>(h, s.I, R, ws.h16, ws.hexp); break;
+        case 2: hpack_kernel<2><<<nb, 256, 0, st>>>(h, s.I, R, ws.h16, ws.hexp); break;
+        case 4: hpack_kernel<4><<<nb, 256, 0, st>>>(h, s.I, R, ws.h16, ws.hexp); break;
+        case 8: hpack_kernel<8><<<nb, 256, 0, st>>>(h, s.I, R, ws.h16, ws.hexp); break;
+        default: hpack_kernel<0><<<nb, 256, 0, st>>>(h, s.I, R, ws.h16, ws.hexp); break;
+    }
+    return hipGetLastError();
+}
+
 // Batches of at most kDecodeMaxTokens tokens (routed by the small-batch
 // routing, which lists the active experts) take the one-tile variant.
 hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
@@ -433,9 +467,7 @@ hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
 
 hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
                                   const Workspace &ws, hipStream_t st) {
-    vq_hpack_kernel<<<T * s.K, 256, 0, st>>>(static_cast<const float *>(ws.h), s.I, ws.h16,
-                                             ws.hexp);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
     const int ns = (s.H + 511) / 512;
     if (T <= kDecodeMaxTokens)

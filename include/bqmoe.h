@@ -87,12 +87,15 @@ enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2, MOE_FMT_VQ13 = 3 };
  * kernels at every batch size, and forcing DECODE on them returns
  * MOE_EUNSUPPORTED.
  *
- * Numerics of the grouped-GEMM kernels: MXFP4 weights are exact in bf16 and
- * the intermediate h enters the down projection as an exact bf16 pair
- * (hi + lo); VQ13R8 weights enter as fp16(Cb + Rb) (one rounding, relative
+ * Numerics of the grouped-GEMM kernels: MXFP4 gate/up weights are exact in
+ * bf16; MXFP4 down weights enter in fp16 as E2M1 * 2^(e - b), b the largest
+ * exponent of their 16-row group (exact while a group's exponents span at
+ * most 13, beyond that only bits 2^-14 below the group's largest weights are
+ * lost); VQ13R8 weights enter as fp16(Cb + Rb) (one rounding, relative
  * error <= 2^-11; VQ13 weights enter as Cb exactly) with the row gain
- * applied in fp32, and x and h as fp16 rows scaled by an exact power of two
- * per row (relative error <= 2^-11 for h).  The VQ decode kernels take Cb and
+ * applied in fp32.  The intermediate h of both formats, and x for VQ, enter
+ * as fp16 rows scaled by an exact power of two per row (relative error
+ * <= 2^-11).  The VQ decode kernels take Cb and
  * Rb unrounded and the activations as above.  All products accumulate in
  * fp32. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };

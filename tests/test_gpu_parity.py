@@ -94,6 +94,24 @@ def test_prefill_scaled_tokens_tiny(torch_dev):
     _full_check(torch_dev, wl, PRE)
 
 
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+@pytest.mark.parametrize("lo,hi", [(110, 123), (100, 140)], ids=["span13", "span40"])
+def test_wide_exponent_spans(torch_dev, path, lo, hi):
+    """E8M0 exponents spread over 13 and over 40 binades in every row group.
+    The prefill down GEMM scales each group's weights by its largest exponent
+    into fp16: exact up to a span of 13, beyond that the lowest blocks lose
+    bits far below the output tolerance."""
+    wl = W.TINY.replace(tokens=16 if path == DEC else 48, seed=15, exp_lo=lo, exp_hi=hi)
+    _full_check(torch_dev, wl, path)
+
+
+def test_prefill_long_down_rows(torch_dev):
+    """Intermediate 2176: 68 scale tiles per down row, more than one pass of
+    the per-group exponent scan, and 17 K steps."""
+    wl = W.TINY.replace(tokens=40, seed=16, inter=2176, experts=4, name="tiny_i2176")
+    _full_check(torch_dev, wl, PRE)
+
+
 def test_all_experts_active_k8(torch_dev):
     wl = W.TINY.replace(top_k=8, name="tiny_k8")
     for path in (DEC, PRE):
