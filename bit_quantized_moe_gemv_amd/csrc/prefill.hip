@@ -107,6 +107,22 @@ __device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
     return d > 0 ? __uint_as_float((uint32_t)d << 23) : 0.f;
 }
 
+// Token chunks of block half th of an expert with ne tokens: chunk i of the
+// expert (64 tokens) belongs to half i%2.  For 64 < ne <= 128 the two halves
+// take an even split in 16-token tiles instead (the first half gets the odd
+// tile), so the sibling blocks that stream the same weight slice run at the
+// same pace and the second one finds the slice in L2.
+struct ChunkPlan {
+    int c0, nt0;  // first chunk's start and size (nt0 < 0: 64-token chunks throughout)
+};
+__device__ __forceinline__ ChunkPlan chunk_plan(int ne, int th) {
+    if (ne > 64 && ne <= 128) {
+        const int split = 16 * (((ne + 15) / 16 + 1) / 2);
+        return {th ? split : 0, th ? ne - split : split};
+    }
+    return {64 * th, -1};
+}
+
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  Grid: E * I/128 * 2 blocks of 4 waves; two blocks share
 // a CU (60 KiB of LDS and at most 256 registers per wave each), so every SIMD
@@ -285,8 +301,9 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
     const int sg = (lane >> 2) & 3;
     const int sgrp = (sg < 2 ? 0 : ngate) + 8 * b + 2 * wave + (sg & 1);
 
-    for (int c0 = 64 * th; c0 < ne; c0 += 128) {
-        const int nt = min(64, ne - c0);
+    const ChunkPlan plan = chunk_plan(ne, th);
+    for (int c0 = plan.c0; c0 < ne; c0 += 128) {
+        const int nt = plan.nt0 >= 0 ? plan.nt0 : min(64, ne - c0);
         const int mt = (nt + 15) / 16;
         // the token row this lane copies: token 16w + l/4 of the chunk
         const uint16_t *brow =
@@ -296,7 +313,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > 64 * th) stage_barrier();  // previous chunk's readers are done with the rings
+        if (c0 > plan.c0) stage_barrier();  // previous chunk's readers are done with the rings
         int unused[kGuGroups];
         gu_pipeline<false>(ex, ex + (size_t)I * H, kt, H / 128, grp, sgrp, lds, brow, wave, lane,
                            mt, acc, unused);
@@ -350,8 +367,9 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
     for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
     const int sgrp = 16 * b + 4 * wave + ((lane >> 2) & 3);
 
-    for (int c0 = 64 * th; c0 < ne; c0 += 128) {
-        const int nt = min(64, ne - c0);
+    const ChunkPlan plan = chunk_plan(ne, th);
+    for (int c0 = plan.c0; c0 < ne; c0 += 128) {
+        const int nt = plan.nt0 >= 0 ? plan.nt0 : min(64, ne - c0);
         const int mt = (nt + 15) / 16;
         const uint16_t *brow = h16 + (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
         f32x4 acc[kGuGroups][4];
@@ -359,7 +377,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > 64 * th) stage_barrier();
+        if (c0 > plan.c0) stage_barrier();
         int bexp[kGuGroups];
         gu_pipeline<true>(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, sgrp, lds, brow,
                           wave, lane, mt, acc, bexp);
