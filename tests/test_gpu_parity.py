@@ -75,11 +75,12 @@ def test_zero_router_sends_all_tokens_to_first_experts(torch_dev, path):
     assert got["counts"][:wl.top_k].tolist() == [wl.tokens] * wl.top_k
 
 
-@pytest.mark.parametrize("t", [64, 65, 80, 97, 128, 129])
+@pytest.mark.parametrize("t", [64, 65, 80, 97, 128, 129, 241])
 def test_prefill_expert_token_counts_around_two_chunks(torch_dev, t):
     """A zero router gives experts 0..k-1 all t tokens: counts at and around
     the 64/128-token boundaries where an expert's tokens are split between two
-    blocks (an even split in 16-token tiles for 64 < t <= 128)."""
+    blocks (an even split in 16-token tiles for 64 < t <= 128, 64-token chunks
+    alternating between the blocks above)."""
     wl = W.TINY.replace(tokens=t, seed=200 + t)
     wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
     got, _, _ = _full_check(torch_dev, wl, PRE, wr=wr)
