@@ -32,18 +32,6 @@ __device__ __forceinline__ void fp4x32_to_bf16(const uint4 v, float scale, bf16x
     }
 }
 
-// fp32 pairs of a 16-byte fp4 block: out[b] = columns (2b, 2b+1) * scale.
-__device__ __forceinline__ void fp4x32_to_f32(const uint4 v, float scale, f32x2 *out) {
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        out[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], scale, 0);
-        out[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], scale, 1);
-        out[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], scale, 2);
-        out[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[i], scale, 3);
-    }
-}
-
 constexpr int kRing = 4;  // 1 KiB wave loads kept in flight per wave
 
 // Global loads below never sit under a divergent branch: predicated loads make

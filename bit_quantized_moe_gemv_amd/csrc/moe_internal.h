@@ -99,12 +99,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // E8M0 exponent byte (1..254) as the fp32 scale 2^(e-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
 // Four packed fp4 bytes (one dword) -> eight bf16, each times `scale`.
