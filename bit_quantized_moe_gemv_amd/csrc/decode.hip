@@ -60,11 +60,13 @@ __device__ __forceinline__ void reg_fence(uint4 &v) {
 // LDS-only barrier, so the weight stream is never stalled by them.  h is
 // written in fp32, in route-position order.
 // ---------------------------------------------------------------------------
-// With R1 (a single token) the block routes the token itself: wave 0 selects
-// the top-k of the router logits (the same one-wave selection as the routing
-// kernel), every block takes the slot-th selected expert in ascending order,
-// and block (0, 0) publishes the routing for the down kernel and
-// moe_layer_routing.  This replaces a separate routing launch.
+// With R1 (a single token) the blocks route the token themselves, which
+// replaces a separate routing launch: wave 0 of every streaming block finds the
+// selected set of experts (wave_topk_set: ballots only, no ordering or
+// weights) and takes the slot-th selected expert in ascending order; one block
+// of an extra row runs the full ordered selection with its weights (the same
+// one-wave selection as the routing kernel) and publishes the routing for the
+// down kernel and moe_layer_routing.
 template <int NJ, int TC, bool R1, int RS>
 __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
@@ -77,21 +79,29 @@ __global__ __launch_bounds__(256) void decode_gateup_mxfp4(
     const int slot = blockIdx.x;
     int e, p0, ne;
     if (R1) {
+        if (blockIdx.y == gridDim.y - 1) {
+            // the extra row (dispatched after the streaming blocks, which keep
+            // their even spread over the XCDs): block (0, last) publishes the
+            // ordered routing and its weights for the down kernel and
+            // moe_layer_routing while the other blocks stream
+            if (slot == 0 && threadIdx.x < 64) {
+                int sel[kMaxTopK];
+                float wt[kMaxTopK];
+                wave_topk(logits, E, K, sigmoid, sel, wt);
+                int pos[kMaxTopK];
+                single_token_positions(sel, K, pos);
+                publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active,
+                                     counts, offsets);
+            }
+            return;
+        }
         __shared__ int s_e;
-        if (threadIdx.x < 64) {
-            int sel[kMaxTopK];
-            float wt[kMaxTopK];
-            wave_topk(logits, E, K, sigmoid, sel, wt);
-            int pos[kMaxTopK];
-            single_token_positions(sel, K, pos);
-            int mine = sel[0];
-#pragma unroll
-            for (int s2 = 0; s2 < kMaxTopK; ++s2)
-                if (s2 < K && pos[s2] == slot) mine = sel[s2];
-            if (threadIdx.x == 0) s_e = mine;
-            if (blockIdx.x == 0 && blockIdx.y == 0)
-                publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active, counts,
-                                     offsets);
+        if (threadIdx.x < 64) {  // which expert: only the selected set is needed here
+            float lv[4];
+            topk_load(logits, E, lv);
+            uint64_t m[4];
+            wave_topk_set(lv, E, K, m);
+            if (threadIdx.x == 0) s_e = topk_set_nth(m, slot);
         }
         lds_barrier();
         e = s_e;
@@ -346,8 +356,9 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
 template <int NJ, int TC, bool R1, int RS>
 static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                 const Workspace &ws, hipStream_t st) {
+    // a single token gets one more row of blocks: its block (0, last) publishes the routing
     const int slots = min(s.E, T * s.K);
-    dim3 grid(slots, s.I / (16 * RS));
+    dim3 grid(slots, s.I / (16 * RS) + (R1 ? 1 : 0));
     decode_gateup_mxfp4<NJ, TC, R1, RS><<<grid, 256, (size_t)TC * s.H * 2, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.active, ws.offsets, ws.perm,
         static_cast<float *>(ws.h), ws.logits, ws.idx, ws.w, ws.counts, ws.inv,

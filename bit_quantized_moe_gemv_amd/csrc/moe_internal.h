@@ -279,6 +279,74 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int K, bool
     wave_topk_vals(v, E, K, sigmoid, idx, w);
 }
 
+// ---------------------------------------------------------------------------
+// The selected set alone (no order, no weights), for kernels that only need to
+// know which experts a single token uses.  Same selection as wave_topk: the K
+// best by (logit descending, expert index ascending).  The K-th largest key t
+// comes from a bitwise binary search whose counts are wave ballots; the set is
+// every key above t plus the lowest-index experts equal to t.  Wave-uniform
+// scalar work only: no cross-lane data movement besides the ballots.
+// ---------------------------------------------------------------------------
+
+// Order-preserving unsigned key of a float; -0 is first turned into +0, so the
+// two zeros tie (and the index decides), as in key_beats.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Bit l of m[j] is set when expert l + 64j is among the K selected (E <= 256).
+__device__ inline void wave_topk_set(const float (&lv)[4], int E, int K, uint64_t (&m)[4]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // past E: key 0, below every finite logit's key
+        k[j] = lane + 64 * j < E ? f32_order_key(lv[j]) : 0u;
+    uint32_t t = 0;  // the largest t with at least K keys >= t: the K-th largest key
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = t | (1u << b);
+        int n = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) n += __popcll(__ballot(k[j] >= c));
+        if (n >= K) t = c;
+    }
+    int need = K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m[j] = __ballot(k[j] > t);
+        need -= __popcll(m[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // ties at t: lowest expert indices first
+        uint64_t eq = __ballot(k[j] == t && lane + 64 * j < E);
+        while (need > 0 && eq) {
+            const uint64_t low = eq & (~eq + 1);
+            m[j] |= low;
+            eq ^= low;
+            --need;
+        }
+    }
+}
+
+// The r-th (from 0) selected expert in ascending index order, i.e. the expert
+// the counting sort puts at route position r of a single token.
+__device__ inline int topk_set_nth(const uint64_t (&m)[4], int r) {
+    int e = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = __popcll(m[j]);
+        if (!found && r < c) {
+            uint64_t x = m[j];
+            for (int i = 0; i < r; ++i) x &= x - 1;
+            e = 64 * j + __builtin_ctzll(x);
+            found = true;
+        }
+        r -= found ? 0 : c;
+    }
+    return e;
+}
+
 // Route positions of a single token: slot s goes to position pos[s], the rank
 // of its expert among the selected ones (ascending), which is the order the
 // counting sort gives.

@@ -87,6 +87,24 @@ def test_prefill_expert_token_counts_around_two_chunks(torch_dev, t):
     assert got["counts"][:wl.top_k].tolist() == [t] * wl.top_k
 
 
+@pytest.mark.parametrize("experts,k", [(8, 2), (256, 8)])
+def test_single_token_tied_logits(torch_dev, experts, k):
+    """Batch-1 decode with equal logits at the selection boundary: experts
+    whose router rows are identical (and largest) tie, and the lowest indices
+    must win, as must experts 0..k-1 when the router is all zero."""
+    wl = W.TINY.replace(tokens=1, experts=experts, top_k=k, seed=300 + experts,
+                        name=f"tiny_e{experts}_k{k}")
+    x = W.make_x(wl)
+    wr = W.make_router(wl)
+    rng = np.random.default_rng(7)
+    tied = np.sort(rng.choice(experts, size=k + 2, replace=False))
+    wr[tied] = np.abs(wr[0]) * np.sign(W.bf16_bits_to_f32(x[0]).astype(np.float32)) * 3.0
+    got, _, _ = _full_check(torch_dev, wl, DEC, x=x, wr=wr)
+    assert sorted(got["idx"][0].tolist()) == tied[:k].tolist()
+    got, _, _ = _full_check(torch_dev, wl, DEC, x=x, wr=np.zeros_like(wr))
+    assert sorted(got["idx"][0].tolist()) == list(range(k))
+
+
 @pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
 def test_zero_input_gives_zero_output(torch_dev, path):
     wl = W.TINY
