@@ -257,7 +257,11 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, q = lane >> 4;
     const int kh = wave & 1;
-    const int n_active = active[0];
+    // a single token has K distinct experts, and the counting sort puts the
+    // q-th of them (ascending) at route position q: no routing reads are
+    // needed before the h rows can be fetched
+    const bool single = T == 1;
+    const int n_active = single ? K : active[0];
     const int R = T * K;
     // routing weights of the combine, fetched now so their latency is hidden
     const int rr = min(tid, R - 1);
@@ -271,8 +275,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
 
     for (int qs = wave >> 1; qs < n_active; qs += kDnWaves / 2) {
         const int e = active[1 + qs];
-        const int p0 = offsets[e];
-        const int ne = offsets[e + 1] - p0;
+        const int p0 = single ? qs : offsets[e];
+        const int ne = single ? 1 : offsets[e + 1] - p0;
         if (!live) {
             for (int r = 0; r < ne; ++r)
                 if (q == 0) ys[kh][p0 + r][n] = 0.f;
