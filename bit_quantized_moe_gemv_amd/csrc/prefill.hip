@@ -69,6 +69,10 @@ __device__ __forceinline__ void stage_barrier() {
 __device__ __forceinline__ void copy_lds16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
+// The same with 4 bytes per lane (256 B per wave).
+__device__ __forceinline__ void copy_lds4(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
 
 // blockIdx -> (expert, block): the blocks of one expert land on one XCD (the
 // dispatcher deals workgroups round-robin over the 8 XCDs), so the expert's
@@ -145,11 +149,12 @@ constexpr int kGuRing = 3;
 // p ^ ((m/4) % 4).  A copy instruction moves 64 contiguous bytes of each of 16
 // token rows (lane l: token 16w + l/4, position l%4), and the MFMA reads of
 // 16 tokens touch 16 distinct bank groups.
-// Scales: each wave copies those of its own 4 groups (4 replicas of 256 B:
-// [replica][group][tile q][row]), so every wave issues the same loads per step.
+// Scales: each wave copies those of its own 4 groups, 256 B per step laid out
+// [group][tile q][row] (lane l moves rows 4(l%4)..+3 of tile (l/4)%4 of group
+// l/16), so every wave issues the same loads per step.
 struct GuLds {
     uint8_t b[kGuRing][4][64][64];          // 16 KiB per slot
-    uint8_t sc[kGuRing][kGuWaves][4][256];  // 4 KiB per slot
+    uint8_t sc[kGuRing][kGuWaves][256];     // 1 KiB per slot
 };
 
 // MFMAs of one step for one wave: 4 K steps x 4 groups x mt token tiles.  The
@@ -166,7 +171,7 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
     float scale[kGuGroups];
 #pragma unroll
     for (int g = 0; g < kGuGroups; ++g) {
-        const uint32_t e = lds.sc[slot][wave][0][64 * g + 16 * q + n];
+        const uint32_t e = lds.sc[slot][wave][64 * g + 16 * q + n];
         scale[g] = F16 ? e8m0_rel_f32(e, b[g]) : e8m0_to_f32(e);
     }
     V8 a[2][kGuGroups];
@@ -213,13 +218,15 @@ __device__ __forceinline__ uint32_t byte_max(uint32_t w) {
 
 template <bool F16>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
-                                            int nsuper, const int (&grp)[kGuGroups], int sgrp,
+                                            int nsuper, const int (&grp)[kGuGroups],
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
                                             int mt, f32x4 (&acc)[kGuGroups][4],
                                             int (&b)[kGuGroups]) {
     constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
     uint4 ring[kGuRing][kGuGroups];
     uint32_t goff[kGuGroups];
+    const uint32_t soff =
+        (uint32_t)(((size_t)grp[lane >> 4] * kt + ((lane >> 2) & 3)) * 16) + 4 * (lane & 3);
 #pragma unroll
     for (int g = 0; g < kGuGroups; ++g)
         goff[g] = (uint32_t)((size_t)grp[g] * kt * 256) + lane * 16;
@@ -230,8 +237,8 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             copy_lds16(brow + 128 * J + 8 * (4 * i + swz), lds.b[slot][i][16 * wave]);
-        // scales: lane l copies group (l/4)%4 (row group sgrp), tile 4J + l%4
-        copy_lds16(scales + ((size_t)sgrp * kt + 4 * J + (lane & 3)) * 16, lds.sc[slot][wave][0]);
+        // scales: lane l copies rows 4(l%4)..+3 of tile 4J + (l/4)%4 of group l/16
+        copy_lds4(scales + soff + (size_t)J * 64, lds.sc[slot][wave]);
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
             ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
@@ -297,9 +304,6 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
     int grp[kGuGroups];
 #pragma unroll
     for (int g = 0; g < kGuGroups; ++g) grp[g] = (g < 2 ? 0 : ngate) + 8 * b + 2 * wave + (g & 1);
-    // the scale copy's lane l covers the wave's group (l/4)%4
-    const int sg = (lane >> 2) & 3;
-    const int sgrp = (sg < 2 ? 0 : ngate) + 8 * b + 2 * wave + (sg & 1);
 
     const ChunkPlan plan = chunk_plan(ne, th);
     for (int c0 = plan.c0; c0 < ne; c0 += 128) {
@@ -315,8 +319,8 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > plan.c0) stage_barrier();  // previous chunk's readers are done with the rings
         int unused[kGuGroups];
-        gu_pipeline<false>(ex, ex + (size_t)I * H, kt, H / 128, grp, sgrp, lds, brow, wave, lane,
-                           mt, acc, unused);
+        gu_pipeline<false>(ex, ex + (size_t)I * H, kt, H / 128, grp, lds, brow, wave, lane, mt,
+                           acc, unused);
         // epilogue: lane holds rows 4q..4q+3 of each group for token 16t + n;
         // gate group i pairs with up group 2 + i
 #pragma unroll
@@ -365,7 +369,6 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
     int grp[kGuGroups];
 #pragma unroll
     for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
-    const int sgrp = 16 * b + 4 * wave + ((lane >> 2) & 3);
 
     const ChunkPlan plan = chunk_plan(ne, th);
     for (int c0 = plan.c0; c0 < ne; c0 += 128) {
@@ -379,8 +382,8 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > plan.c0) stage_barrier();
         int bexp[kGuGroups];
-        gu_pipeline<true>(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, sgrp, lds, brow,
-                          wave, lane, mt, acc, bexp);
+        gu_pipeline<true>(codes, codes + (size_t)H * I / 2, kt, I / 128, grp, lds, brow, wave,
+                          lane, mt, acc, bexp);
         int hs[4];  // row exponents of the lane's tokens, fetched together
 #pragma unroll
         for (int t = 0; t < 4; ++t) hs[t] = hexp[p0 + c0 + min(16 * t + n, nt - 1)] - 127;
