@@ -18,7 +18,9 @@
 namespace bqmoe {
 
 constexpr int kDecTC = 4;  // routes (tokens) per pass through the staged operand
-constexpr int kDecRS = 4;  // row groups a gate/up block streams one after another
+// row groups a gate/up block streams one after another: one token / up to 16 tokens
+constexpr int kDecRS1 = 2;
+constexpr int kDecRS = 4;
 
 // bf16 pairs of a 16-byte fp4 block: out[b] = columns (2b, 2b+1) * scale.
 __device__ __forceinline__ void fp4x32_to_bf16(const uint4 v, float scale, bf16x2 *out) {
@@ -373,8 +375,9 @@ static hipError_t gateup_launch(const Shape &s, int T, const uint16_t *x, const 
 template <int NJ>
 static hipError_t gateup_launch_tc(const Shape &s, int T, const uint16_t *x,
                                    const uint8_t *packed, const Workspace &ws, hipStream_t st) {
-    constexpr int RS = NJ >= 32 ? 1 : kDecRS;  // (the unrolled stream grows with RS * NJ)
-    return T == 1 ? gateup_launch<NJ, 1, true, RS>(s, T, x, packed, ws, st)
+    // (the unrolled stream grows with RS * NJ)
+    constexpr int RS1 = NJ >= 32 ? 1 : kDecRS1, RS = NJ >= 32 ? 1 : kDecRS;
+    return T == 1 ? gateup_launch<NJ, 1, true, RS1>(s, T, x, packed, ws, st)
                   : gateup_launch<NJ, kDecTC, false, RS>(s, T, x, packed, ws, st);
 }
 
