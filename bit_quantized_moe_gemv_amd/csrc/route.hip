@@ -310,11 +310,33 @@ hipError_t launch_topk(const Shape &s, int T, const Workspace &ws, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// large batches: one block per expert.  Each block builds the full expert
-// histogram, takes its own offset, then compacts its routes in route order
-// (a stable counting sort split by expert; no inter-block communication).
+// large batches: one block per expert.  Thread t owns a contiguous run of
+// kPermPer routes (per pass of 256 * kPermPer), so a block-wide exclusive scan
+// of the per-thread match counts gives every route of expert e its place in
+// route order (a stable counting sort split by expert).  The expert's offset
+// is the number of routes with a smaller expert index, counted the same way;
+// block 0 also builds the histogram (counts, offsets, the active list).  With
+// R <= 256 * kPermPer (2048 tokens at k = 8) the routes are read once, into
+// registers, with all loads in flight together.
 // ---------------------------------------------------------------------------
-constexpr int kPermPerThread = 8;
+constexpr int kPermPer = 64;
+constexpr int kPermPass = 256 * kPermPer;
+
+// the pass's expert indices of thread tid: routes [r0, r0 + kPermPer), padded with E
+__device__ __forceinline__ void perm_load(const int32_t *__restrict__ idx, int R, int E, int r0,
+                                          int (&v)[kPermPer]) {
+#pragma unroll
+    for (int i = 0; i < kPermPer; i += 4) {
+        const int r = r0 + i;
+        if (r + 3 < R) {
+            const int4 q = *reinterpret_cast<const int4 *>(idx + r);
+            v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[i + k] = r + k < R ? idx[r + k] : E;
+        }
+    }
+}
 
 __global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict__ idx, int R, int E,
                                                       int32_t *__restrict__ counts,
@@ -326,47 +348,59 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict_
     __shared__ int s_scan[16];
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
-    for (int i = tid; i < kMaxExperts; i += blockDim.x) hist[i] = 0;
-    __syncthreads();
-    for (int r = tid; r < R; r += blockDim.x) atomicAdd(&hist[idx[r]], 1);
-    __syncthreads();
-    int total;
-    const int my = (tid < E) ? hist[tid] : 0;
-    const int excl = block_exclusive_scan(my, &total, s_scan);
-    __shared__ int s_base;
-    if (tid == e) s_base = excl;
     if (e == 0) {
-        if (tid < E) { counts[tid] = my; offsets[tid] = excl; }
-        if (tid == 0) offsets[E] = total;
+        for (int i = tid; i < kMaxExperts; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+    }
+    int v[kPermPer];
+    const bool one = R <= kPermPass;
+    // offset of expert e: routes with a smaller expert index (block 0 also
+    // counts every expert)
+    int below = 0;
+    for (int b = 0; b < R; b += kPermPass) {
+        perm_load(idx, R, E, b + tid * kPermPer, v);
+#pragma unroll
+        for (int i = 0; i < kPermPer; ++i) {
+            below += v[i] < e;
+            if (e == 0 && v[i] < E) atomicAdd(&hist[v[i]], 1);
+        }
+    }
+    int base;
+    {
+        int tot;
+        block_exclusive_scan(below, &tot, s_scan);
+        base = tot;
     }
     if (e == 0) {
+        __syncthreads();
+        int total;
+        const int my = (tid < E) ? hist[tid] : 0;
+        const int excl = block_exclusive_scan(my, &total, s_scan);
+        if (tid < E) { counts[tid] = my; offsets[tid] = excl; }
+        if (tid == 0) offsets[E] = total;
         int n_active;
         const int flag = (tid < E && my > 0) ? 1 : 0;
         const int apos = block_exclusive_scan(flag, &n_active, s_scan);
         if (flag) active[1 + apos] = tid;
         if (tid == 0) active[0] = n_active;
     }
-    __syncthreads();
-    const int base = s_base;
-    int running = 0;
-    const int chunk = blockDim.x * kPermPerThread;
-    for (int b = 0; b < R; b += chunk) {
-        const int r0 = b + tid * kPermPerThread;
-        int flags = 0, n = 0;
+    // compaction: this thread's matches, in route order
+    int running = base;
+    for (int b = 0; b < R; b += kPermPass) {
+        const int r0 = b + tid * kPermPer;
+        if (!one) perm_load(idx, R, E, r0, v);
+        uint64_t m = 0;
 #pragma unroll
-        for (int q = 0; q < kPermPerThread; ++q) {
-            const int r = r0 + q;
-            if (r < R && idx[r] == e) { flags |= 1 << q; ++n; }
-        }
+        for (int i = 0; i < kPermPer; ++i) m |= (uint64_t)(v[i] == e) << i;
         int tot;
-        int pos = block_exclusive_scan(n, &tot, s_scan) + running + base;
-#pragma unroll
-        for (int q = 0; q < kPermPerThread; ++q)
-            if (flags & (1 << q)) {
-                perm[pos] = r0 + q;
-                inv[r0 + q] = pos;
-                ++pos;
-            }
+        int pos = block_exclusive_scan(__popcll(m), &tot, s_scan) + running;
+        while (m) {
+            const int i = __builtin_ctzll(m);
+            m &= m - 1;
+            perm[pos] = r0 + i;
+            inv[r0 + i] = pos;
+            ++pos;
+        }
         running += tot;
     }
 }

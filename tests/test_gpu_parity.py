@@ -119,6 +119,13 @@ def test_prefill_ragged_medium(torch_dev):
     _full_check(torch_dev, wl, PRE)
 
 
+def test_prefill_more_routes_than_one_permute_pass(torch_dev):
+    """8300 tokens at k = 2: 16,600 routes, more than the 16,384 the
+    permutation kernel holds in registers, so it takes its two-pass path."""
+    wl = W.TINY.replace(tokens=8300, seed=17, name="tiny_t8300")
+    _full_check(torch_dev, wl, PRE)
+
+
 def test_prefill_scaled_tokens_tiny(torch_dev):
     wl = W.TINY.replace(tokens=64, seed=13, scaled_tokens=4, token_scale=64.0)
     _full_check(torch_dev, wl, PRE)
