@@ -8,7 +8,7 @@
 // weights and multiplies it with the expert's tokens, 64 at a time.
 //
 // Shape of a kernel: blocks of four waves with 4 row groups (16 weight rows
-// each) per wave, at most 256 registers and about 60-72 KiB of LDS per block,
+// each) per wave, at most 256 registers and 51 KiB of LDS per block,
 // so two independent blocks share each CU and every SIMD runs two waves that
 // hide each other's memory and barrier stalls.  Per K step of 128 columns each
 // wave issues, in a fixed order, its copies of the B stage and of its groups'
@@ -129,7 +129,7 @@ __device__ __forceinline__ ChunkPlan chunk_plan(int ne, int th) {
 
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  Grid: E * I/128 * 2 blocks of 4 waves; two blocks share
-// a CU (60 KiB of LDS and at most 256 registers per wave each), so every SIMD
+// a CU (51 KiB of LDS and at most 256 registers per wave each), so every SIMD
 // runs two independent waves that hide each other's stalls.  Block (b, half
 // th) of expert e owns gate row groups 8b..8b+7 and their up partners and the
 // expert's tokens in 64-token chunks th, th+2, ...; wave w computes gate
