@@ -278,7 +278,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode only")
     ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "vq_decode",
