@@ -195,6 +195,9 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
     };
     load_b(0, 0);
     dequant(0, 0);
+    // raised issue priority while this wave has MFMAs to issue, so the
+    // co-resident block's waves, busy with loads and barriers, yield to it
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int cur = ks & 1;
@@ -210,6 +213,7 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
                     acc[g][t] = mfma_op(a[cur][g], bv[cur][t], acc[g][t]);
             }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 __device__ __forceinline__ uint32_t byte_max(uint32_t w) {
