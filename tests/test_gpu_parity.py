@@ -272,3 +272,35 @@ def test_sigmoid_routing_extreme_logits(torch_dev):
 
 def test_mimo_decode_batch1_sigmoid(torch_dev):
     _sampled_check(torch_dev, W.DECODE.replace(routing=SIGMOID), DEC, [0])
+
+
+def test_handles_on_concurrent_streams(torch_dev):
+    """Handles share no state: four layers (batch-1 decode, 16-token decode,
+    grouped MXFP4, grouped VQ13R8), each with its own workspace, run
+    interleaved on two streams of default priority and give, bit for bit, what
+    each gives alone on the default stream."""
+    import bit_quantized_moe_gemv_amd as bq
+    torch = torch_dev
+    cases = [(W.TINY.replace(tokens=1, name="t1"), DEC), (W.TINY, DEC),
+             (W.TINY.replace(tokens=200, seed=18), PRE), (W.TINY_VQ, PRE)]
+    runs = []
+    for wl, path in cases:
+        x = torch.from_numpy(W.make_x(wl).view(np.int16)).cuda().view(torch.bfloat16)
+        wr = torch.from_numpy(W.make_router(wl)).cuda()
+        pk = torch.from_numpy(W.make_experts(wl)).cuda()
+        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, wl.tokens, wl.fmt, path)
+        alone = layer.forward(x, wr, pk).clone()
+        runs.append((layer, x, wr, pk, alone))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):  # a handle stays on one stream (calls sharing a handle serialize)
+        for i, (layer, x, wr, pk, _) in enumerate(runs):
+            s = streams[i % 2]
+            with torch.cuda.stream(s):
+                outs.append((i, layer.forward(x, wr, pk, stream=s)))
+    torch.cuda.synchronize()
+    for i, out in outs:
+        assert torch.equal(out, runs[i][4]), f"case {i} differs on a concurrent stream"
+    for layer, *_ in runs:
+        layer.close()
