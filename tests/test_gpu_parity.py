@@ -304,3 +304,45 @@ def test_handles_on_concurrent_streams(torch_dev):
         assert torch.equal(out, runs[i][4]), f"case {i} differs on a concurrent stream"
     for layer, *_ in runs:
         layer.close()
+
+
+def test_forward_in_a_captured_graph(torch_dev):
+    """A forward makes no host syncs, allocations or memsets, so it can be
+    captured into a graph: every replay (with eager forwards and
+    synchronisations in between, and after the input is overwritten in
+    place) matches the eager result bit for bit."""
+    import bit_quantized_moe_gemv_amd as bq
+    torch = torch_dev
+    cases = [(W.TINY.replace(tokens=1, name="t1"), DEC), (W.TINY, DEC),
+             (W.TINY.replace(tokens=200, seed=19), PRE), (W.TINY_VQ, PRE)]
+    for wl, path in cases:
+        x = torch.from_numpy(W.make_x(wl).view(np.int16)).cuda().view(torch.bfloat16)
+        x2 = torch.from_numpy(W.make_x(wl.replace(seed=wl.seed + 50)).view(np.int16)).cuda() \
+            .view(torch.bfloat16)
+        wr = torch.from_numpy(W.make_router(wl)).cuda()
+        pk = torch.from_numpy(W.make_experts(wl)).cuda()
+        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, wl.tokens, wl.fmt, path)
+        ref1 = layer.forward(x, wr, pk).clone()
+        ref2 = layer.forward(x2, wr, pk).clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer.forward(x, wr, pk, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        xin = x.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = layer.forward(xin, wr, pk)
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref1), f"{wl.name}: replay {rep} differs"
+            layer.forward(x2, wr, pk)  # eager work between replays
+            torch.cuda.synchronize()
+        xin.copy_(x2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref2), f"{wl.name}: replay after the input changed differs"
+        del g
+        layer.close()
