@@ -209,13 +209,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     }
 }
 
+constexpr int kRsWaves = 2;  // waves (experts) per block of the small-batch router
+
 template <int TT, int MAXG>
-__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(64 * kRsWaves) void router_small_kernel(const uint16_t *__restrict__ x,
                                                            const float *__restrict__ wr, int T,
                                                            int H, int E,
                                                            float *__restrict__ logits) {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int e = blockIdx.y * kRsWaves + (threadIdx.x >> 6);
     const int t0 = blockIdx.x * TT;
     if (e >= E) return;
     const int groups = H >> 8;
@@ -253,19 +255,21 @@ template <int TT>
 static void router_small_launch(const Shape &s, dim3 grid, hipStream_t st, const uint16_t *x,
                                 const float *wr, int T, float *logits) {
     const int g = s.H / 256;
-    if (g <= 1) router_small_kernel<TT, 1><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else if (g <= 4) router_small_kernel<TT, 4><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else if (g <= 16) router_small_kernel<TT, 16><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else router_small_kernel<TT, 32><<<grid, 256, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    constexpr int nt = 64 * kRsWaves;
+    if (g <= 1) router_small_kernel<TT, 1><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else if (g <= 4) router_small_kernel<TT, 4><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else if (g <= 16) router_small_kernel<TT, 16><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    else router_small_kernel<TT, 32><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
 }
 
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
                                      const Workspace &ws, hipStream_t st, bool route_single) {
     if (T < 1 || T > kDecodeMaxTokens || s.H / 256 > 32) return hipErrorInvalidValue;
+    const int ey = (s.E + kRsWaves - 1) / kRsWaves;
     if (T == 1)
-        router_small_launch<1>(s, dim3(1, (s.E + 3) / 4), st, x, wr, T, ws.logits);
+        router_small_launch<1>(s, dim3(1, ey), st, x, wr, T, ws.logits);
     else
-        router_small_launch<4>(s, dim3((T + 3) / 4, (s.E + 3) / 4), st, x, wr, T, ws.logits);
+        router_small_launch<4>(s, dim3((T + 3) / 4, ey), st, x, wr, T, ws.logits);
     hipError_t e = hipGetLastError();
     // a single token is routed by the batch-1 gate/up kernel unless route_single
     if (e != hipSuccess || (T == 1 && !route_single)) return e;

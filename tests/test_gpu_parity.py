@@ -87,6 +87,19 @@ def test_prefill_expert_token_counts_around_two_chunks(torch_dev, t):
     assert got["counts"][:wl.top_k].tolist() == [t] * wl.top_k
 
 
+@pytest.mark.parametrize("hidden,inter", [(512, 512), (1024, 1024), (2048, 256), (8192, 128)])
+@pytest.mark.parametrize("t", [1, 6])
+def test_decode_kernel_shapes(torch_dev, hidden, inter, t):
+    """The decode kernels are instantiated per hidden size (gate/up: 256-column
+    super-steps per K slice, row groups per block) and per intermediate size
+    (down: super-steps per K half); every hidden size from 512 to 8192 and every
+    down instantiation runs here, at one token (routing inside the gate/up
+    kernel) and at six."""
+    wl = W.TINY.replace(tokens=t, hidden=hidden, inter=inter, experts=6, top_k=3,
+                        seed=400 + hidden // 256 + t, name=f"dec_h{hidden}_i{inter}_t{t}")
+    _full_check(torch_dev, wl, DEC)
+
+
 @pytest.mark.parametrize("experts,k", [(8, 2), (256, 8)])
 def test_single_token_tied_logits(torch_dev, experts, k):
     """Batch-1 decode with equal logits at the selection boundary: experts
