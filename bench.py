@@ -50,15 +50,16 @@ def _src_hash(*names):
     return h.hexdigest()
 
 
-def _traffic(kernel: str, src: str, launches_units: float):
+def _traffic(kernel: str, src: tuple, launches_units: float):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    if there is none or the kernel source changed since it was taken."""
+    if there is none or the kernel's sources (its file and the shared device
+    header) changed since it was taken."""
     path = os.path.join(PROFILE_DIR, f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256") != _src_hash(src):
+    if d.get("source_sha256") != _src_hash(*src):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -334,7 +335,7 @@ def main():
     achieved = alg["gateup_bytes"] / (gu_us * 1e-6) / 1e9
     roof = {"kernel": "decode_gateup_mxfp4", "bound": "hbm", "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": _traffic("decode_gateup_mxfp4", "decode.hip", 1),
+            "traffic": _traffic("decode_gateup_mxfp4", ("decode.hip", "moe_internal.h"), 1),
             "algorithmic_bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": gu_us}
     step_gbs = alg["step_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
     extra = {"decode_t1": {**dec, "step_algorithmic_bytes": alg["step_bytes"],

@@ -284,7 +284,9 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int K, bool
 // know which experts a single token uses.  Same selection as wave_topk: the K
 // best by (logit descending, expert index ascending).  The K-th largest key t
 // comes from a bitwise binary search whose counts are wave ballots; the set is
-// every key above t plus the lowest-index experts equal to t.  Wave-uniform
+// every key above t plus the lowest-index experts equal to t.  The search stops
+// as soon as a prefix of t has exactly K keys at or above it (the usual case
+// after the sign, exponent and a few mantissa bits).  Wave-uniform
 // scalar work only: no cross-lane data movement besides the ballots.
 // ---------------------------------------------------------------------------
 
@@ -308,7 +310,16 @@ __device__ inline void wave_topk_set(const float (&lv)[4], int E, int K, uint64_
         int n = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) n += __popcll(__ballot(k[j] >= c));
-        if (n >= K) t = c;
+        if (n >= K) {
+            t = c;
+            // exactly K keys >= c: they are the selection, and no tie can
+            // straddle it (n is wave-uniform, so is the early exit)
+            if (n == K) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m[j] = __ballot(k[j] >= c);
+                return;
+            }
+        }
     }
     int need = K;
 #pragma unroll
