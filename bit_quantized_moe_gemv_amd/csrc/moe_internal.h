@@ -305,6 +305,9 @@ __device__ inline void wave_topk_set(const float (&lv)[4], int E, int K, uint64_
     for (int j = 0; j < 4; ++j)  // past E: key 0, below every finite logit's key
         k[j] = lane + 64 * j < E ? f32_order_key(lv[j]) : 0u;
     uint32_t t = 0;  // the largest t with at least K keys >= t: the K-th largest key
+    // unrolled: each step's threshold is t | constant, with t and the counts
+    // in scalar registers
+#pragma unroll
     for (int b = 31; b >= 0; --b) {
         const uint32_t c = t | (1u << b);
         int n = 0;
