@@ -223,15 +223,18 @@ class Bench:
 def algorithmic(wl, distinct, T):
     """Algorithmic bytes / flops of the gate/up and down kernels and the whole
     step.  Per expert: MXFP4 gate/up 2*I*H*17/32 bytes and down H*I*17/32
-    bytes; VQ13R8 21/64 byte per weight plus an fp16 gain per row."""
+    bytes; VQ13R8 21/64 byte per weight (VQ13 13/64) plus an fp16 gain per row."""
     H, I, k = wl.hidden, wl.inter, wl.top_k
     R = T * k
-    if wl.fmt == W_FMT_VQ:
-        gu_e = 2 * I * H * 21 // 64 + 2 * (2 * I)
-        dn_e = H * I * 21 // 64 + 2 * H
-    else:
+    if wl.fmt in (W_FMT_VQ, W_FMT_VQ13):
+        bits = 21 if wl.fmt == W_FMT_VQ else 13  # index bits per 8-weight vector
+        gu_e = 2 * I * H * bits // 64 + 2 * (2 * I)
+        dn_e = H * I * bits // 64 + 2 * H
+    elif wl.fmt == W_FMT_MXFP4:
         gu_e = 2 * I * H * 17 // 32
         dn_e = H * I * 17 // 32
+    else:
+        raise ValueError(f"unknown expert format {wl.fmt}")
     gateup_bytes = distinct * gu_e + T * H * 2 + R * I * 4
     down_bytes = distinct * dn_e + R * I * 4 + T * H * 4
     step_bytes = distinct * (gu_e + dn_e) + wl.experts * H * 4 + T * H * 2 + T * H * 4
@@ -241,7 +244,7 @@ def algorithmic(wl, distinct, T):
                 gateup_flops=flops_gu, down_flops=flops_dn, step_flops=flops_gu + flops_dn)
 
 
-W_FMT_VQ = 2
+W_FMT_MXFP4, W_FMT_VQ, W_FMT_VQ13 = 1, 2, 3
 
 
 def prefill_report(pre, a):
