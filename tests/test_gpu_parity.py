@@ -100,6 +100,30 @@ def test_decode_kernel_shapes(torch_dev, hidden, inter, t):
     _full_check(torch_dev, wl, DEC)
 
 
+@pytest.mark.parametrize("base,sizes,paths", [
+    (W.TINY, (16, 17, 16, 1), (DEC, PRE, DEC, DEC)),
+    (W.TINY_VQ, (1, 2, 1), (DEC, PRE, DEC)),
+], ids=["mxfp4", "vq13r8"])
+def test_auto_path_choice(torch_dev, base, sizes, paths):
+    """With no forced path one handle serves every batch size up to its
+    maximum: the decode kernels up to the threshold (16 tokens for MXFP4, one
+    for VQ) and the grouped GEMM above it, switching back and forth between
+    calls; both sides of the threshold agree with the oracle."""
+    from gpu_harness import Runner, log
+    import oracle
+    run = Runner(base, 0, max_tokens=32)
+    for t, want in zip(sizes, paths):
+        wl = base.replace(tokens=t, seed=600 + t)
+        log(f"case {base.name} AUTO T={t}")
+        x, wr = W.make_x(wl), W.make_router(wl)
+        got = run.run(x, wr)
+        assert got["path"] == want, (t, got["path"])
+        _routing_exact(got, oracle.route(x, wr, wl.top_k, wl.routing), wl)
+        ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k,
+                                 run.packed_host, x, wr, routing=wl.routing)
+        check_output(got["out"], ref["out"])
+
+
 @pytest.mark.parametrize("experts,k", [(8, 2), (256, 8)])
 def test_single_token_tied_logits(torch_dev, experts, k):
     """Batch-1 decode with equal logits at the selection boundary: experts
