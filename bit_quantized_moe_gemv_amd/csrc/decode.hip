@@ -164,11 +164,10 @@ __global__ __launch_bounds__(128 * KW) void decode_gateup_mxfp4(
         // further on.  The ring runs across row-group boundaries.
         constexpr int JJ = RS * NW;
         const uint32_t rstride = (uint32_t)(kt * 256), sstride = (uint32_t)(kt * 16);
-        constexpr int KR = kRing;
-        uint4 ring[KR];
-        uint32_t sring[KR];
+        uint4 ring[kRing];
+        uint32_t sring[kRing];
 #pragma unroll
-        for (int j = 0; j < KR && j < JJ; ++j) {
+        for (int j = 0; j < kRing && j < JJ; ++j) {
             ring[j] = ld16(cbase, (j / NW) * rstride + coff + (j % NW) * 1024);
             sring[j] = sbase[(j / NW) * sstride + soff + (j % NW) * 64];
         }
@@ -186,19 +185,19 @@ __global__ __launch_bounds__(128 * KW) void decode_gateup_mxfp4(
 #pragma unroll
                 for (int tt = 0; tt < TC; ++tt) acc[tt] = 0.f;
             }
-            uint4 wv = ring[jj % KR];
-            uint32_t sv = sring[jj % KR];
+            uint4 wv = ring[jj % kRing];
+            uint32_t sv = sring[jj % kRing];
             reg_fence(wv);
             reg_fence(sv);
             const float sc = e8m0_to_f32(sv);
-            if (jj + KR < JJ) {
-                const int jn = jj + KR;
+            if (jj + kRing < JJ) {
+                const int jn = jj + kRing;
                 uint32_t o = (jn / NW) * rstride + coff + (jn % NW) * 1024;
                 uint32_t so = (jn / NW) * sstride + soff + (jn % NW) * 64;
                 reg_fence(o);
                 reg_fence(so);
-                ring[jj % KR] = ld16(cbase, o);
-                sring[jj % KR] = sbase[so];
+                ring[jj % kRing] = ld16(cbase, o);
+                sring[jj % kRing] = sbase[so];
             }
             bf16x2 w2[16];
             fp4x32_to_bf16(wv, sc, w2);
