@@ -186,18 +186,23 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     if (wave == 0) {
         float lv[4];
         topk_load(logits, E, lv);
-        int sel[kMaxTopK], pos[kMaxTopK];
-        float wt[kMaxTopK];
-        wave_topk_vals(lv, E, K, sigmoid, sel, wt);
-        single_token_positions(sel, K, pos);
-        int e0 = sel[0];
+        if (blockIdx.x == 0) {  // the ordered selection with its weights, published
+            int sel[kMaxTopK], pos[kMaxTopK];
+            float wt[kMaxTopK];
+            wave_topk_vals(lv, E, K, sigmoid, sel, wt);
+            single_token_positions(sel, K, pos);
+            int e0 = sel[0];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-            if (s < K && pos[s] == p) e0 = sel[s];
-        if (lane == 0) lds.expert = e0;
-        if (blockIdx.x == 0)
+            for (int s = 0; s < kMaxTopK; ++s)
+                if (s < K && pos[s] == p) e0 = sel[s];
+            if (lane == 0) lds.expert = e0;
             publish_single_token(sel, wt, pos, E, K, idx_out, w_out, perm, inv, active, counts,
                                  offsets);
+        } else {  // the set only: route position p holds its p-th expert in index order
+            uint64_t m[4];
+            wave_topk_set(lv, E, K, m);
+            if (lane == 0) lds.expert = topk_set_nth(m, p);
+        }
     } else {
         uint4 bv[kBookLoads];
         load_books<kVdThreads - 64, RES>(packed, tid - 64, bv);
