@@ -22,8 +22,9 @@
 //    groups of 16 rows).  Each wave streams GW groups over TJ tiles of K; the
 //    partial dot products meet in LDS and the block applies the row gains,
 //    2^s_x and SwiGLU, writing h (fp32, route-position order).  Every block
-//    selects the top-k from the router logits itself (one wave); block 0
-//    publishes the routing.
+//    finds its expert from the router logits itself (one wave, the selected
+//    set only); block 0 runs the ordered top-k with its weights and publishes
+//    the routing.
 //  * vq_dec_down: block = one output row group (16 rows) for all k routes.
 //    Each wave streams one route's tiles over a quarter of K; the routes go
 //    through in two phases of four, h of the phase's routes staged in LDS as
