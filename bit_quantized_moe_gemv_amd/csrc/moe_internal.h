@@ -19,6 +19,7 @@ constexpr int kWave = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 256;
 constexpr int kDecodeMaxTokens = 16;
+constexpr int kMaxHidden = 8192;
 constexpr int kVqEntries = 8192;
 constexpr int kVqResEntries = 256;
 constexpr size_t kVqBooksBytes = (size_t)(kVqEntries + kVqResEntries) * 8 * 2;  // VQ13R8
@@ -92,6 +93,8 @@ hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
 hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
                                   const Workspace &ws, hipStream_t st);
 hipError_t launch_combine(const Shape &s, int T, const Workspace &ws, float *out, hipStream_t st);
+// measurement aid: one streaming read of `bytes` (a multiple of 16) at buf
+hipError_t launch_read_probe(const uint8_t *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
 // ---- device helpers ----
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -200,12 +203,26 @@ __device__ __forceinline__ void cswap(float &va, int &ia, float &vb, int &ib) {
     ia = ti;
 }
 
-// The lane's four logits (experts lane + 64j), -inf past E.  Issued as
+// The value a logit is ranked by.  A NaN logit (reachable only from
+// non-finite inputs, e.g. inf - inf inside a router sum of huge activations)
+// ranks as -inf, below every number: both selections below then compare
+// ordinary floats, agree, and never pick an index outside [0, E).
+__host__ __device__ constexpr float selection_value(float v) { return v != v ? -INFINITY : v; }
+
+// Order-preserving unsigned key of a ranked value (after selection_value):
+// a > b as floats iff key(a) > key(b); -0 is first turned into +0, so the two
+// zeros tie (and the index decides), as in key_beats.
+__host__ __device__ constexpr uint32_t f32_order_key(float f) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The lane's four ranked logits (experts lane + 64j), -inf past E.  Issued as
 // unconditional loads (clamped index) so a caller can count them.
 __device__ __forceinline__ void topk_load(const float *__restrict__ l, int E, float (&v)[4]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = l[min(lane + 64 * j, E - 1)];
+    for (int j = 0; j < 4; ++j) v[j] = selection_value(l[min(lane + 64 * j, E - 1)]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         if (lane + 64 * j >= E) v[j] = -INFINITY;
@@ -237,7 +254,7 @@ __device__ inline void wave_topk_vals(const float (&lv)[4], int E, int K, bool s
                 gi = __builtin_amdgcn_readlane(i0, __ffsll((unsigned long long)hit) - 1);
             else                     // equal logits: lowest expert index wins
                 gi = wave_min_i32(v0 == m ? i0 : 0x7FFFFFFF);
-            idx[s] = gi;
+            idx[s] = min(gi, E - 1);  // gi < E whenever k <= E; kept in range regardless
             val[s] = m;
             if (i0 == gi) {  // pop the head
                 v0 = v1; i0 = i1;
@@ -289,13 +306,6 @@ __device__ inline void wave_topk(const float *__restrict__ l, int E, int K, bool
 // after the sign, exponent and a few mantissa bits).  Wave-uniform
 // scalar work only: no cross-lane data movement besides the ballots.
 // ---------------------------------------------------------------------------
-
-// Order-preserving unsigned key of a float; -0 is first turned into +0, so the
-// two zeros tie (and the index decides), as in key_beats.
-__device__ __forceinline__ uint32_t f32_order_key(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Bit l of m[j] is set when expert l + 64j is among the K selected (E <= 256).
 __device__ inline void wave_topk_set(const float (&lv)[4], int E, int K, uint64_t (&m)[4]) {
