@@ -45,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "moe_layer_set_profiling",
     "moe_layer_profile_read",
     "moe_layer_replay_stage",
+    "moe_read_probe",
     "moe_layer_destroy",
     "moe_status_str",
 )
@@ -105,6 +106,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_layer_replay_stage.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, P, P,
                                            ctypes.c_size_t, ctypes.c_int32, P, P]
     lib.moe_layer_replay_stage.restype = ctypes.c_int
+    lib.moe_read_probe.argtypes = [P, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int32,
+                                   ctypes.c_int32, P, P]
+    lib.moe_read_probe.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -140,6 +144,15 @@ def workspace_size(hidden, inter, n_experts, top_k, max_tokens, fmt=MOE_FMT_MXFP
     if rc != MOE_OK:
         raise MoeError(rc, "moe_workspace_size")
     return b.value
+
+
+def read_probe(buf_ptr: int, nbytes: int, copy_stride: int, n_copies: int, reps: int,
+               sink_ptr: int, stream_ptr: int) -> None:
+    """Enqueue `reps` plain streaming reads of nbytes (moe_read_probe)."""
+    rc = load_library().moe_read_probe(buf_ptr, nbytes, copy_stride, n_copies, reps, sink_ptr,
+                                       ctypes.c_void_p(stream_ptr))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_read_probe")
 
 
 def _ptr(t) -> int:
@@ -183,11 +196,40 @@ class MoeLayer:
             raise MoeError(rc, "moe_layer_create")
         self._handle = h
         self._last_T = 0
+        self._packed_bytes = packed_size(hidden, inter, n_experts, top_k, max_tokens, fmt,
+                                         force_path, routing)
 
     @property
     def packed_bytes(self) -> int:
-        return packed_size(self.hidden, self.inter, self.n_experts, self.top_k, self.max_tokens,
-                           self.fmt, self.force_path)
+        return self._packed_bytes
+
+    def _check_args(self, x, router_w, packed, out):
+        """Dtype, layout, shape and device of the tensors handed to the C ABI:
+        the kernels index them by the descriptor's sizes, so a mismatch here
+        would become an out-of-bounds device access."""
+        import torch
+
+        def need(ok, msg):
+            if not ok:
+                raise ValueError(f"MoeLayer.forward: {msg}")
+
+        need(x.dim() == 2 and x.shape[1] == self.hidden and 1 <= x.shape[0] <= self.max_tokens,
+             f"x must be [T, {self.hidden}] with 1 <= T <= {self.max_tokens}, got {tuple(x.shape)}")
+        T = int(x.shape[0])
+        for name, t, dt, shape in (("x", x, torch.bfloat16, (T, self.hidden)),
+                                   ("router_w", router_w, torch.float32,
+                                    (self.n_experts, self.hidden)),
+                                   ("out", out, torch.float32, (T, self.hidden))):
+            need(t.dtype == dt, f"{name} must be {dt}, got {t.dtype}")
+            need(tuple(t.shape) == shape, f"{name} must have shape {shape}, got {tuple(t.shape)}")
+            need(t.is_contiguous(), f"{name} must be contiguous")
+        need(packed.dtype == torch.uint8 and packed.is_contiguous(),
+             "packed must be a contiguous uint8 tensor")
+        need(packed.numel() >= self._packed_bytes,
+             f"packed holds {packed.numel()} bytes, the layer needs {self._packed_bytes}")
+        dev = self.workspace.device
+        for name, t in (("x", x), ("router_w", router_w), ("packed", packed), ("out", out)):
+            need(t.device == dev, f"{name} is on {t.device}, the layer's workspace on {dev}")
 
     def forward(self, x, router_w, packed, out=None, stream=None):
         import torch
@@ -195,6 +237,7 @@ class MoeLayer:
         T = int(x.shape[0])
         if out is None:
             out = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device)
+        self._check_args(x, router_w, packed, out)
         if stream is None:
             stream = torch.cuda.current_stream(x.device)
         rc = self._lib.moe_layer_forward(self._handle, _ptr(x), T, _ptr(router_w), _ptr(packed),

@@ -102,7 +102,9 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
 
 static int check_desc(const moe_layer_desc *d, Shape *s) {
     if (!d) return MOE_EINVAL;
-    if (d->hidden < 256 || d->hidden > 16384 || d->hidden % 256) return MOE_EINVAL;
+    // hidden <= 8192: the small-batch router holds a token's row in registers
+    // (at most 32 groups of 256 columns per wave)
+    if (d->hidden < 256 || d->hidden > kMaxHidden || d->hidden % 256) return MOE_EINVAL;
     if (d->inter < 128 || d->inter > 16384) return MOE_EINVAL;
     if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_EINVAL;
     if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts) return MOE_EINVAL;
@@ -319,6 +321,19 @@ int moe_layer_replay_stage(moe_layer *L, int32_t stage, int32_t reps, const void
             default: e = launch_combine(s, T, ws, out, st); break;
         }
         if (e != hipSuccess) return MOE_EHIP;
+    }
+    return MOE_OK;
+}
+
+int moe_read_probe(const void *buf, size_t bytes, size_t copy_stride, int32_t n_copies,
+                   int32_t reps, uint32_t *sink, void *hip_stream) {
+    if (!aligned16(buf) || bytes < 16 || (bytes & 15u) || (copy_stride & 15u)) return MOE_EINVAL;
+    if (n_copies < 1 || reps < 1 || !sink || ((uintptr_t)sink & 3u)) return MOE_EINVAL;
+    if (n_copies > 1 && copy_stride < bytes) return MOE_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    for (int i = 0; i < reps; ++i) {
+        const uint8_t *p = static_cast<const uint8_t *>(buf) + (size_t)(i % n_copies) * copy_stride;
+        if (launch_read_probe(p, bytes, sink, st) != hipSuccess) return MOE_EHIP;
     }
     return MOE_OK;
 }

@@ -2,9 +2,9 @@
  * bqmoe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer with
  * block-quantized experts.
  *
- * The layer (MiMo-V2.6-Flash-RL shape: 256 routed experts, 8 active per token,
- * no shared expert -- TrevorJS GGUF card, "Architecture notes"; hidden 4096,
- * expert intermediate 2048) computes for every token t
+ * The layer (MiMo-V2.6-Flash-RL shape: every token is routed to 8 of 256
+ * experts and the layer has no shared expert -- TrevorJS GGUF card,
+ * "Architecture notes"; hidden 4096, expert intermediate 2048) computes for every token t
  *
  *   l      = x_t . Wr^T                    fp32 router (F32 router: savrn
  *                                          card, "Quantization targets")
@@ -69,8 +69,8 @@ enum {
  *   Cb[i][d] + Rb[j][d] must be finite in fp16 (|sum| <= 65504).
  *
  * MOE_FMT_VQ13 (the 13-bit stage alone -- Baekpica VQ card, "Recipe": every
- * layer carries it, 32 layers add the residual stage, and the 13-bit stage is
- * byte-identical with and without it): packed = [Cb: 8192 x 8 fp16] then
+ * layer carries it and 32 layers add the residual stage on top, leaving the
+ * 13-bit stage's bytes as they are): packed = [Cb: 8192 x 8 fp16] then
  * n_experts experts of 3*inter*hidden*13/64 + 2*(2*inter + hidden) bytes:
  *   [gu code12][gu plane][gu gain][dn code12][dn plane][dn gain],
  * each region as in MOE_FMT_VQ13R8; weight w[n][8v+d] = gain[n] * Cb[i13][d].
@@ -111,7 +111,7 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 enum { MOE_ROUTE_SOFTMAX = 0, MOE_ROUTE_SIGMOID = 1 };
 
 typedef struct {
-    int32_t hidden;     /* H: multiple of 256 */
+    int32_t hidden;     /* H: multiple of 256, at most 8192 */
     int32_t inter;      /* I: multiple of 128 (MXFP4) or 256 (VQ13R8, VQ13) */
     int32_t n_experts;  /* E: 1..256 */
     int32_t top_k;      /* k: 1..8 and k <= E */
@@ -207,6 +207,18 @@ int moe_layer_profile_read(moe_layer *layer, float *ms, int32_t slots);
 int moe_layer_replay_stage(moe_layer *layer, int32_t stage, int32_t reps, const void *x_bf16,
                            const float *router_w, const void *packed_experts, size_t copy_stride,
                            int32_t n_copies, float *out, void *hip_stream);
+
+/* Measurement aid: the attainable read bandwidth that the weight-streaming
+ * kernels' HBM rates are compared with.  Enqueues `reps` streaming reads of
+ * `bytes` of device memory on hip_stream, read i at buf + (i % n_copies) *
+ * copy_stride (cycling copies keeps the last-level cache from serving them),
+ * each a plain read with 16-byte loads over the whole GPU that writes
+ * nothing (sink: a device uint32, written only with vanishing probability,
+ * so that the loads are kept).  bytes and copy_stride are multiples of 16,
+ * buf 16-byte aligned, copy_stride >= bytes when n_copies > 1.  Returns
+ * MOE_EINVAL on a bad argument, MOE_EHIP if a launch fails. */
+int moe_read_probe(const void *buf, size_t bytes, size_t copy_stride, int32_t n_copies,
+                   int32_t reps, uint32_t *sink, void *hip_stream);
 
 /* Release the handle (not the workspace).  NULL is a no-op. */
 void moe_layer_destroy(moe_layer *layer);

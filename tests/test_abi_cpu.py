@@ -58,7 +58,7 @@ def test_sizes_for_the_mimo_layer(lib):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(hidden=200), dict(hidden=0), dict(inter=96), dict(n_experts=0), dict(n_experts=300),
+    dict(hidden=200), dict(hidden=0), dict(hidden=8448), dict(hidden=16384), dict(inter=96), dict(n_experts=0), dict(n_experts=300),
     dict(top_k=0), dict(top_k=9), dict(top_k=9, n_experts=8), dict(max_tokens=0),
     dict(fmt=7), dict(force_path=5),
 ])
@@ -68,6 +68,13 @@ def test_descriptor_validation(lib, bad):
     with pytest.raises(bq.MoeError) as ei:
         bq.packed_size(**d)
     assert ei.value.status == bq.MOE_EINVAL
+
+
+def test_largest_hidden_accepted(lib):
+    """hidden 8192 is the largest width every path takes (the small-batch
+    router holds a token's row in 32 groups of 256 columns)."""
+    assert bq.packed_size(8192, 128, 8, 2) == 3 * 128 * 8192 * 17 // 32 * 8
+    assert bq.workspace_size(8192, 128, 8, 2, 16) > 0
 
 
 def test_top_k_larger_than_experts_rejected(lib):
@@ -165,3 +172,36 @@ def test_vq13_descriptor_sizes(lib):
     with pytest.raises(bq.MoeError) as ei:
         bq.packed_size(256, 256, 8, 2, fmt=4)
     assert ei.value.status == bq.MOE_EINVAL
+
+
+def test_binding_rejects_mismatched_tensors(lib):
+    """MoeLayer.forward checks dtype, shape, contiguity, byte size and device
+    of every tensor before the C call (the kernels would otherwise index past
+    a too-small or differently laid out buffer).  A CPU workspace suffices:
+    every case here is refused before anything reaches the library, so the
+    checks run on a handle-less instance with a CPU workspace."""
+    import torch
+    layer = bq.MoeLayer.__new__(bq.MoeLayer)
+    layer.hidden, layer.n_experts, layer.max_tokens = 256, 8, 16
+    layer._packed_bytes = bq.packed_size(256, 128, 8, 2)
+    layer.workspace = torch.empty(16, dtype=torch.uint8)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    wr = torch.zeros((8, 256), dtype=torch.float32)
+    pk = torch.zeros(layer.packed_bytes, dtype=torch.uint8)
+    out = torch.zeros((4, 256), dtype=torch.float32)
+    bad = [
+        dict(x=x.float()), dict(x=torch.zeros((4, 512), dtype=torch.bfloat16)),
+        dict(x=torch.zeros((17, 256), dtype=torch.bfloat16)),
+        dict(x=torch.zeros((256, 4), dtype=torch.bfloat16).t()),
+        dict(router_w=wr.half()), dict(router_w=torch.zeros((7, 256))),
+        dict(router_w=torch.zeros((256, 8)).t()),
+        dict(packed=pk[:-1]), dict(packed=pk.view(torch.int8)),
+        dict(out=out.double()), dict(out=torch.zeros((4, 128))),
+        dict(out=torch.zeros((256, 4)).t()),
+    ]
+    for kw in bad:
+        args = dict(x=x, router_w=wr, packed=pk, out=out)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            layer._check_args(args["x"], args["router_w"], args["packed"], args["out"])
+    layer._check_args(x, wr, pk, out)  # the matching set passes
