@@ -7,9 +7,10 @@
  * reader can check every step against the definitions below by eye.
  *
  * What it computes, for every token t (MiMo-V2.6-Flash-RL routed-expert
- * layer: 256 routed experts, 8 active, no shared expert -- TrevorJS GGUF
- * card, "Architecture notes"; router kept in F32 -- savrn mixed-quant card,
- * first paragraph and "Quantization targets"):
+ * layer: each token uses 8 of 256 routed experts and the layer has no
+ * shared expert -- TrevorJS GGUF card, "Architecture notes"; router kept in
+ * F32 -- savrn mixed-quant card, first paragraph and "Quantization
+ * targets"):
  *
  *   l[e]   = sum_h x[t,h] * Wr[e,h]                 (fp32, canonical order)
  *   idx    = the k experts with the largest l, ties to the lower index
@@ -285,9 +286,9 @@ static double or_sigmoid(double v) {
  * routing -- TrevorJS card, "Architecture notes"), sigma(l_s) divided by the
  * sum of sigma over the k selected logits.  (The logistic form is used for
  * logits above -700; below that every sigma underflows in double and the
- * ratio is undefined here.)  (8 active experts per token -- TrevorJS card,
- * "Architecture notes"; "eight routes per processed token" -- ProCreations IQ3
- * card, "Calibration".) */
+ * ratio is undefined here.)  (k = 8 selected experts per token -- TrevorJS
+ * card, "Architecture notes"; the calibration counts of the ProCreations IQ3
+ * card, "Calibration", confirm 8 routes for each token.) */
 int oracle_topk(const float *logits, int64_t T, int64_t E, int64_t k, int routing, int32_t *idx,
                 double *w) {
     if (routing != 0 && routing != 1) return -1;

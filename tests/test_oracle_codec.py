@@ -165,8 +165,8 @@ def test_vq_zero_residual_equals_r13_only(oracle_lib):
 def test_vq13_layer_is_the_13_bit_stage(oracle_lib):
     """A VQ13 layer (no residual stage) holding the 13-bit stage of a VQ13R8
     layer whose residual book is zero decodes to the same weights and gives
-    the same layer output bit for bit (the 13-bit stage is byte-identical
-    with and without the residual stage: Baekpica VQ card, "Recipe").  The
+    the same layer output bit for bit (adding the residual stage leaves the
+    13-bit stage's bytes unchanged: Baekpica VQ card, "Recipe").  The
     VQ13 buffer is the VQ13R8 one with the residual regions cut out."""
     rng = np.random.default_rng(4)
     cb = rng.standard_normal((8192, 8)).astype(np.float16)

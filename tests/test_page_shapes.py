@@ -1,6 +1,6 @@
 """The layer shape is pinned by totals the model cards print
 (tests/golden/page_payloads.txt): hidden 4096, expert intermediate 2048,
-256 routed experts, 8 active, 47 MoE layers."""
+top-8 routing over 256 experts, 47 MoE layers."""
 
 import os
 

@@ -5,8 +5,8 @@ benchmark.  It draws random numbers and lays them out in the packed byte
 formats; it performs none of the layer's arithmetic (no decoding, no routing,
 no matrix products).
 
-Shapes follow the MiMo-V2.6-Flash-RL model cards: 256 routed experts, 8 active
-per token, no shared expert (TrevorJS GGUF card, "Architecture notes"); expert
+Shapes follow the MiMo-V2.6-Flash-RL model cards: each token is routed to 8 of
+256 experts, with no shared expert (TrevorJS GGUF card, "Architecture notes"); expert
 intermediate width 2048 (Baekpica VQ card, "Why 13 bits plus an 8-bit
 residual"); hidden width 4096 (implied by the routed-parameter and payload
 totals on the savrn mixed-quant card, "Memory metrics").  Experts are stored as
