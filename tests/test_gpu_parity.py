@@ -216,24 +216,54 @@ def _mimo_layer(seed):
     return _LAYERS[seed]
 
 
-def _sampled_check(torch_dev, wl, path, sample):
+def covering_sample(idx, n_min, must=()):
+    """Token rows in which every expert that some token routes to appears at
+    least once (a greedy set cover over the routing idx [T, k]), together with
+    the rows in `must`, topped up with evenly spaced rows to at least n_min
+    rows (sorted)."""
+    idx = np.asarray(idx)
+    t, _ = idx.shape
+    member = np.zeros((t, int(idx.max()) + 1), dtype=bool)
+    member[np.arange(t)[:, None], idx] = True
+    chosen = set(int(m) for m in must)
+    uncovered = member.any(axis=0)
+    for m in chosen:
+        uncovered &= ~member[m]
+    while uncovered.any():
+        best = int(np.argmax((member & uncovered).sum(axis=1)))
+        chosen.add(best)
+        uncovered &= ~member[best]
+    for m in np.linspace(0, t - 1, num=n_min).astype(int):
+        if len(chosen) >= n_min:
+            break
+        chosen.add(int(m))
+    return sorted(chosen)
+
+
+def _sampled_check(torch_dev, wl, path, sample, packed=None):
+    """Routing of every token bit for bit; the output on the rows `sample`
+    names (a list, or a function of the oracle's routing that returns one)."""
     from gpu_harness import Runner, log
     import oracle
-    log(f"case {wl.name} T={wl.tokens} path={path} sample={list(sample)}")
+    log(f"case {wl.name} T={wl.tokens} path={path}")
     x, wr = W.make_x(wl), W.make_router(wl)
-    packed = _mimo_layer(wl.seed)
+    packed = _mimo_layer(wl.seed) if packed is None else packed
     run = Runner(wl, path, packed=packed)
     got = run.run(x, wr)
     log("  gpu done; oracle routing")
     ref_route = oracle.route(x, wr, wl.top_k, wl.routing)
+    if path != 0:
+        assert got["path"] == path
     _routing_exact(got, ref_route, wl)
-    log("  routing exact; oracle outputs")
+    if callable(sample):
+        sample = sample(ref_route)
+    log(f"  routing exact; oracle outputs of {len(sample)} rows: {list(sample)}")
     ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, packed, x, wr,
                              tokens=sample, routing=wl.routing)
     l2, mx = check_output(got["out"][np.asarray(sample)], ref["out"])
     log(f"  worst sampled row: rel l2 {l2:.2e}, max/rms {mx:.2e}")
     assert np.all(np.isfinite(got["out"]))
-    return got
+    return got, sample
 
 
 def test_mimo_decode_batch1(torch_dev):
@@ -241,17 +271,60 @@ def test_mimo_decode_batch1(torch_dev):
 
 
 def test_mimo_verify_batch16_skewed(torch_dev):
-    got = _sampled_check(torch_dev, W.VERIFY, DEC, [0, 5, 15])
+    """Every row of the 16-token verify batch (skewed routing)."""
+    got, _ = _sampled_check(torch_dev, W.VERIFY, DEC, list(range(16)))
     n_distinct = int((got["counts"] > 0).sum())
     assert 40 <= n_distinct <= 128
 
 
+@pytest.mark.parametrize("t", [3, 8])
+def test_mimo_verify_widths_decode_path(torch_dev, t):
+    """Every row of the 3-token (MTP drafts) and 8-token (drafter block)
+    verify widths of the sweep, on the decode kernels at the MiMo shape."""
+    wl = W.VERIFY.replace(tokens=t, name=f"mimo_verify_t{t}_skewed")
+    _sampled_check(torch_dev, wl, DEC, list(range(t)))
+
+
 def test_mimo_prefill_2048(torch_dev):
+    """The 2048-token prefill: routing of every token bit for bit; outputs on
+    at least 64 rows chosen so that every routed expert's weights meet some
+    sampled token, including all 20 tokens scaled by 64."""
     wl = W.PREFILL
     scaled = W.scaled_token_ids(wl)
-    sample = sorted(set(scaled[:3].tolist()) | {0, 1000, 2047})
-    got = _sampled_check(torch_dev, wl, PRE, sample)
+    got, sample = _sampled_check(
+        torch_dev, wl, PRE, lambda r: covering_sample(r["idx"], 64, must=scaled))
     assert got["counts"].sum() == wl.tokens * wl.top_k
+    assert set(scaled.tolist()) <= set(sample) and len(sample) >= 64
+    assert set(np.unique(got["idx"][sample])) == set(np.nonzero(got["counts"])[0])
+
+
+def test_overflowing_logits_route_in_range(torch_dev):
+    """Activations at the bf16 maximum with opposite signs in the two halves of
+    the row drive every router partial sum to +inf or -inf, so every logit is
+    NaN (inf - inf).  A NaN ranks below every number, so the selection takes
+    the lowest expert indices, [0, k), on every path (batch-1 MXFP4 and VQ
+    decode, grouped GEMM), and the kernels never see an index outside [0, E)."""
+    from gpu_harness import Runner, log
+    import oracle
+    cases = [(W.TINY.replace(tokens=1, name="tiny_t1_nan"), DEC),
+             (W.TINY.replace(tokens=1, experts=256, top_k=8, name="tiny_e256_t1_nan"), DEC),
+             (W.TINY.replace(tokens=3, name="tiny_t3_nan"), DEC),
+             (W.TINY.replace(tokens=20, name="tiny_t20_nan"), PRE),
+             (W.TINY_VQ.replace(tokens=1, name="tiny_vq_t1_nan"), DEC)]
+    for wl, path in cases:
+        log(f"case {wl.name} path={path}")
+        x = np.empty((wl.tokens, wl.hidden), dtype=np.uint16)
+        x[:, :wl.hidden // 2] = 0x7F7F   # +3.39e38
+        x[:, wl.hidden // 2:] = 0xFF7F   # -3.39e38
+        wr = np.ones((wl.experts, wl.hidden), dtype=np.float32)
+        run = Runner(wl, path)
+        got = run.run(x, wr)
+        ref = oracle.route(x, wr, wl.top_k, wl.routing)
+        assert np.all(np.isnan(got["logits"])) and np.all(np.isnan(ref["logits"]))
+        want = np.tile(np.arange(wl.top_k, dtype=np.int32), (wl.tokens, 1))
+        assert np.array_equal(got["idx"], want) and np.array_equal(ref["idx"], want)
+        for name in ("counts", "offsets", "perm"):
+            assert np.array_equal(got[name], ref[name]), name
 
 
 @pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])

@@ -80,19 +80,24 @@ def test_tiny_vq_determinism(torch_dev):
 
 def test_mimo_vq_prefill_2048(torch_dev):
     """The full VQ13R8 layer (hidden 4096, intermediate 2048, 256 experts,
-    top-8, 2048 tokens) on sampled token rows."""
-    from gpu_harness import Runner, log
-    import oracle
+    top-8, 2048 tokens): routing of every token bit for bit; outputs on at
+    least 64 rows chosen so that every routed expert's codes meet some sampled
+    token."""
+    from test_gpu_parity import _sampled_check, covering_sample
     wl = W.VQ_PREFILL
-    sample = [0, 1, 777, 1500, 2047]
-    log(f"case {wl.name} T={wl.tokens} sample={sample}")
-    x, wr = W.make_x(wl), W.make_router(wl)
-    run = Runner(wl, PRE)
-    got = run.run(x, wr)
-    _routing_exact(got, oracle.route(x, wr, wl.top_k), wl)
-    assert got["counts"].sum() == wl.tokens * wl.top_k
-    ref = oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k,
-                             run.packed_host, x, wr, tokens=sample)
-    l2, mx = check_output(got["out"][np.asarray(sample)], ref["out"])
-    log(f"  worst sampled row: rel l2 {l2:.2e}, max/rms {mx:.2e}")
-    assert np.all(np.isfinite(got["out"]))
+    got, sample = _sampled_check(torch_dev, wl, PRE, lambda r: covering_sample(r["idx"], 64),
+                                 packed=W.make_experts(wl))
+    assert got["counts"].sum() == wl.tokens * wl.top_k and len(sample) >= 64
+    assert set(np.unique(got["idx"][sample])) == set(np.nonzero(got["counts"])[0])
+
+
+def test_mimo_vq_verify_t16(torch_dev):
+    """The VQ13R8 16-token verify batch the benchmark times: the MiMo-shaped
+    VQ13R8 layer, the skewed verify router and tokens, the AUTO path (the
+    one-token-tile grouped GEMM over the active experts); every row."""
+    from test_gpu_parity import _sampled_check
+    wl = W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed")
+    got, _ = _sampled_check(torch_dev, wl, AUTO, list(range(16)),
+                            packed=W.make_experts(W.VQ_PREFILL))
+    assert got["path"] == PRE
+    assert 40 <= int((got["counts"] > 0).sum()) <= 128
