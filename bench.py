@@ -64,8 +64,32 @@ def _traffic(kernel: str, src: tuple, launches_units: float):
     return d.get("hbm_bytes_per_launch")
 
 
-def measured_peaks(torch):
-    """Attainable peaks on this machine: a device-to-device copy and a bf16 GEMM."""
+def read_probe_gbs(torch, bq, nbytes, n_copies, reps):
+    """Plain streaming read (moe_read_probe) of nbytes, cycling n_copies
+    device copies so the last-level cache does not serve them: GB/s over
+    `reps` back-to-back reads, timed with HIP events on the probe's stream."""
+    stride = (nbytes + 255) // 256 * 256
+    buf = torch.ones(stride * n_copies, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    bq.read_probe(buf.data_ptr(), nbytes, stride, n_copies, max(4, reps // 10), sink.data_ptr(),
+                  st.cuda_stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    bq.read_probe(buf.data_ptr(), nbytes, stride, n_copies, reps, sink.data_ptr(), st.cuda_stream)
+    e1.record(st)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del buf
+    torch.cuda.empty_cache()
+    return round(nbytes / (us * 1e-6) / 1e9, 1), round(us, 3)
+
+
+def measured_peaks(torch, bq, step_bytes):
+    """Attainable peaks on this machine: a device-to-device copy, plain streaming
+    reads (of 2 GiB, and of one decode step's footprint over 8 copies), and a
+    bf16 GEMM."""
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -93,7 +117,11 @@ def measured_peaks(torch):
     tflops = 2 * m ** 3 * it / (time.perf_counter() - t0) / 1e12
     del x, y
     torch.cuda.empty_cache()
-    return {"copy_gbs": round(copy_gbs, 1), "bf16_matmul_tflops": round(tflops, 1)}
+    big_gbs, _ = read_probe_gbs(torch, bq, 2 << 30, 1, 20)
+    step_gbs, step_us = read_probe_gbs(torch, bq, step_bytes, 8, 400)
+    return {"copy_gbs": round(copy_gbs, 1), "read_probe_gbs_2gib": big_gbs,
+            "read_probe_gbs_decode_step": step_gbs, "read_probe_decode_step_bytes": step_bytes,
+            "read_probe_decode_step_us": step_us, "bf16_matmul_tflops": round(tflops, 1)}
 
 
 class Bench:
@@ -104,6 +132,8 @@ class Bench:
         t0 = time.perf_counter()
         self.host_layer = W.make_experts(base)
         log(f"  {time.perf_counter() - t0:.1f}s; copying {args.layers} device copies")
+        self.input_hashes = {f"{base.name}.packed_experts": W.sha256(self.host_layer),
+                             f"{base.name}.router_w": W.sha256(W.make_router(base))}
         self.layers = self._copies(self.host_layer, args.layers)
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
@@ -156,6 +186,9 @@ class Bench:
             x = W.make_x(wl, tokens=T * cnt, stream_offset=1 + off)
             xs.append(torch.from_numpy(x.view("int16")).to("cuda").view(torch.bfloat16))
         xall = torch.cat(xs).view(n_batches, T, wl.hidden)
+        if wl.name == W.DECODE.name:
+            self.input_hashes[f"{wl.name}.x_all_steps"] = W.sha256(
+                xall.view(torch.int16).cpu().numpy())
         wr = torch.from_numpy(W.make_router(wl)).to("cuda")
         layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt, path,
                             routing=wl.routing)
@@ -180,6 +213,18 @@ class Bench:
         elapsed = time.perf_counter() - t0
         res = {"steps": steps, "warmup": warmup, "ms_per_step": elapsed * 1e3 / steps,
                "tokens_per_s": steps * T / elapsed, "path": layer.last_path()}
+        # the same steps again with a HIP event between consecutive steps on
+        # the forward's stream: the median step interval
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(self.stream)
+        for i in range(steps):
+            rc = layer.forward_raw(xp[warmup + i], T, wp, lp[(warmup + i) % L], op, st)
+            if rc != 0:
+                raise bq.MoeError(rc, "moe_layer_forward")
+            evs[i + 1].record(self.stream)
+        evs[-1].synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        res["event_median_ms_per_step"] = round(per[steps // 2], 5)
         # routing statistics of the last step (distinct experts streamed)
         r = layer.routing()
         counts = r.counts.cpu()
@@ -261,19 +306,59 @@ def prefill_report(pre, a):
     }
 
 
-def cpu_baseline(host_layer, W, n_tokens):
+def cpu_baseline(host_layer, W, n_tokens, runs):
+    """The oracle on `runs` independent batches of n_tokens decode tokens of
+    the benchmarked layer: the median rate."""
     import oracle
 
     wl = W.DECODE
-    x = W.make_x(wl, tokens=n_tokens, stream_offset=999)
     wr = W.make_router(wl)
-    t0 = time.perf_counter()
-    oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, host_layer, x, wr)
-    dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+    rates, secs = [], []
+    for r in range(runs):
+        x = W.make_x(wl, tokens=n_tokens, stream_offset=999 + r)
+        t0 = time.perf_counter()
+        oracle.moe_forward(wl.fmt, wl.hidden, wl.inter, wl.experts, wl.top_k, host_layer, x, wr)
+        dt = time.perf_counter() - t0
+        rates.append(n_tokens / dt)
+        secs.append(round(dt, 2))
+    med = sorted(rates)[runs // 2]
+    return {"value": round(med, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{n_tokens} decode tokens of the MiMo-shaped MXFP4 layer "
-                      f"(fp32 router, top-8, 8 experts in float64 each), {dt:.1f} s"}
+            "sample": f"median of {runs} runs of {n_tokens} decode tokens each of the MiMo-shaped "
+                      f"MXFP4 layer (fp32 router, top-8, 8 experts in float64 each); run times "
+                      f"{secs} s",
+            "runs_tokens_per_s": [round(v, 3) for v in rates]}
+
+
+def host_info():
+    """CPU model and core counts from /proc/cpuinfo (physical cores = distinct
+    (physical id, core id) pairs)."""
+    model, cores, logical = None, set(), 0
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "processor":
+                    logical += 1
+                elif k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model or platform.processor() or platform.machine(),
+            "cpu_physical_cores": len(cores) or None, "cpu_logical_cpus": logical or os.cpu_count(),
+            "cpu_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+            else None}
 
 
 def main():
@@ -282,7 +367,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=12, help="oracle tokens per run")
+    ap.add_argument("--cpu-runs", type=int, default=5, help="oracle runs (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode only")
     ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "vq_decode",
@@ -385,12 +471,15 @@ def main():
         extra["vq_prefill_t2048"] = prefill_report(
             vq, algorithmic(W.VQ_PREFILL, W.VQ_PREFILL.experts, 2048))
     if not args.no_peaks:
-        extra["measured_peaks"] = measured_peaks(torch)
+        extra["measured_peaks"] = measured_peaks(torch, bq, alg["step_bytes"])
+        rp = extra["measured_peaks"]["read_probe_gbs_decode_step"]
+        roof["frac_of_read_probe"] = round(achieved / rp, 4)
+        extra["decode_t1"]["step_frac_of_read_probe"] = round(step_gbs / rp, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_tokens} decode tokens")
-        cpu = cpu_baseline(b.host_layer, W, args.cpu_tokens)
+        log(f"cpu baseline: oracle, {args.cpu_runs} runs of {args.cpu_tokens} decode tokens")
+        cpu = cpu_baseline(b.host_layer, W, args.cpu_tokens, args.cpu_runs)
 
     line = {
         "metric": METRIC,
@@ -411,7 +500,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
-        "host": {"cpu": platform.processor() or platform.machine(), "gpu": torch.cuda.get_device_name(0)},
+        "host": {**host_info(), "gpu": torch.cuda.get_device_name(0)},
+        "inputs_sha256": b.input_hashes,
     }
     print(json.dumps(line), flush=True)
 
