@@ -35,7 +35,7 @@ static void prof_release(moe_layer *L) {
 // Runs one launcher, bracketed by the slot's event pair when profiling.
 template <class F>
 static hipError_t staged(moe_layer *L, int slot, int stage, hipStream_t st, F &&launch) {
-    if (slot < 0) return launch();
+    if (!L || slot < 0) return launch();
     hipEvent_t *ev = &L->prof_ev[((size_t)slot * MOE_N_STAGES + stage) * 2];
     hipError_t e = hipEventRecord(ev[0], st);
     if (e == hipSuccess) e = launch();
@@ -144,6 +144,65 @@ static int check_desc(const moe_layer_desc *d, Shape *s) {
 
 static bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
+// The path a forward of T tokens takes (MOE_PATH_DECODE or MOE_PATH_PREFILL),
+// or MOE_EINVAL when a forced decode path cannot take T tokens.
+static int choose_path(const Shape &s, int force_path, int T) {
+    int path = force_path;
+    if (path == MOE_PATH_AUTO)
+        path = (T <= decode_max_tokens(s) && decode_supported(s)) ? MOE_PATH_DECODE
+                                                                 : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_DECODE && T > decode_max_tokens(s)) return MOE_EINVAL;
+    return path;
+}
+
+// The kernel sequence of one forward pass on stream st.  L (may be null) and
+// slot (-1: none) select the profiling events around each stage.
+static hipError_t enqueue_forward(moe_layer *L, int slot, const Shape &s, const Workspace &ws,
+                                  int path, const uint16_t *x, int T, const float *router_w,
+                                  const uint8_t *packed, float *out, hipStream_t st) {
+    hipError_t err = hipSuccess;
+    if (path == MOE_PATH_DECODE) {
+        err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
+            return launch_router_route_small(s, x, router_w, T, ws, st, false);
+        });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_GATEUP, st,
+                         [&] { return launch_decode_gateup(s, T, x, packed, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_DOWN, st,
+                         [&] { return launch_decode_down(s, T, packed, ws, out, st); });
+        return err;
+    }
+    if (T <= kDecodeMaxTokens) {  // small batch (a VQ layer, or a forced path)
+        err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
+            return launch_router_route_small(s, x, router_w, T, ws, st, true);
+        });
+    } else {
+        err = staged(L, slot, MOE_STAGE_ROUTER, st,
+                     [&] { return launch_router(s, x, router_w, T, ws.logits, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
+        if (err == hipSuccess)
+            err = staged(L, slot, MOE_STAGE_PERMUTE, st,
+                         [&] { return launch_permute(s, T, ws, st); });
+    }
+    const bool vq = is_vq_format(s.fmt);
+    if (err == hipSuccess)
+        err = staged(L, slot, MOE_STAGE_GATEUP, st, [&] {
+            return vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
+                      : launch_prefill_gateup(s, T, x, packed, ws, st);
+        });
+    if (err == hipSuccess)
+        err = staged(L, slot, MOE_STAGE_DOWN, st, [&] {
+            return vq ? launch_vq_prefill_down(s, T, packed, ws, st)
+                      : launch_prefill_down(s, T, packed, ws, st);
+        });
+    if (err == hipSuccess)
+        err = staged(L, slot, MOE_STAGE_COMBINE, st,
+                     [&] { return launch_combine(s, T, ws, out, st); });
+    return err;
+}
+
 extern "C" {
 
 int moe_packed_size(const moe_layer_desc *desc, size_t *bytes) {
@@ -195,63 +254,18 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
     if (!aligned16(x_bf16) || !aligned16(router_w) || !aligned16(packed_experts) ||
         !aligned16(out))
         return MOE_EINVAL;
-    int path = L->desc.force_path;
-    if (path == MOE_PATH_AUTO)
-        path = (T <= decode_max_tokens(L->shape) && decode_supported(L->shape)) ? MOE_PATH_DECODE
-                                                                             : MOE_PATH_PREFILL;
-    if (path == MOE_PATH_DECODE && T > decode_max_tokens(L->shape)) return MOE_EINVAL;
-    const Shape &s = L->shape;
-    const Workspace &ws = L->ws;
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
-    const uint8_t *packed = static_cast<const uint8_t *>(packed_experts);
-
+    const int path = choose_path(L->shape, L->desc.force_path, T);
+    if (path < 0) return path;
     int slot = -1;
     if (L->prof_slots > 0) {
         slot = L->prof_next;
         L->prof_next = (L->prof_next + 1) % L->prof_slots;
         for (int i = 0; i < MOE_N_STAGES; ++i) L->prof_ran[(size_t)slot * MOE_N_STAGES + i] = 0;
     }
-    hipError_t err = hipSuccess;
-    if (path == MOE_PATH_DECODE) {
-        err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
-            return launch_router_route_small(s, x, router_w, T, ws, st, false);
-        });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_GATEUP, st,
-                         [&] { return launch_decode_gateup(s, T, x, packed, ws, st); });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_DOWN, st,
-                         [&] { return launch_decode_down(s, T, packed, ws, out, st); });
-    } else {
-        if (T <= kDecodeMaxTokens) {  // small batch (a VQ layer, or a forced path)
-            err = staged(L, slot, MOE_STAGE_ROUTER, st, [&] {
-                return launch_router_route_small(s, x, router_w, T, ws, st, true);
-            });
-        } else {
-            err = staged(L, slot, MOE_STAGE_ROUTER, st,
-                         [&] { return launch_router(s, x, router_w, T, ws.logits, st); });
-            if (err == hipSuccess)
-                err = staged(L, slot, MOE_STAGE_SELECT, st, [&] { return launch_topk(s, T, ws, st); });
-            if (err == hipSuccess)
-                err = staged(L, slot, MOE_STAGE_PERMUTE, st,
-                             [&] { return launch_permute(s, T, ws, st); });
-        }
-        const bool vq = is_vq_format(s.fmt);
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_GATEUP, st, [&] {
-                return vq ? launch_vq_prefill_gateup(s, T, x, packed, ws, st)
-                          : launch_prefill_gateup(s, T, x, packed, ws, st);
-            });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_DOWN, st, [&] {
-                return vq ? launch_vq_prefill_down(s, T, packed, ws, st)
-                          : launch_prefill_down(s, T, packed, ws, st);
-            });
-        if (err == hipSuccess)
-            err = staged(L, slot, MOE_STAGE_COMBINE, st,
-                         [&] { return launch_combine(s, T, ws, out, st); });
-    }
+    const hipError_t err = enqueue_forward(L, slot, L->shape, L->ws, path,
+                                           static_cast<const uint16_t *>(x_bf16), T, router_w,
+                                           static_cast<const uint8_t *>(packed_experts), out,
+                                           static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) return MOE_EHIP;
     L->last_T = T;
     L->last_path = path;
