@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "moe_layer_profile_read",
     "moe_layer_replay_stage",
     "moe_read_probe",
+    "moe_forward_noalloc",
     "moe_layer_destroy",
     "moe_status_str",
 )
@@ -109,6 +110,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_read_probe.argtypes = [P, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int32,
                                    ctypes.c_int32, P, P]
     lib.moe_read_probe.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [D, P, ctypes.c_int32, P, P, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -153,6 +156,17 @@ def read_probe(buf_ptr: int, nbytes: int, copy_stride: int, n_copies: int, reps:
                                        ctypes.c_void_p(stream_ptr))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_read_probe")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def forward_noalloc_raw(desc: moe_layer_desc, x_ptr: int, T: int, router_ptr: int,
+                        packed_ptr: int, out_ptr: int, stream_ptr: int) -> int:
+    """moe_forward_noalloc at pointer level (no checks): the forward pass with
+    the library's own per-GPU workspace array; returns the status code."""
+    return load_library().moe_forward_noalloc(ctypes.byref(desc), x_ptr, T, router_ptr,
+                                              packed_ptr, out_ptr, ctypes.c_void_p(stream_ptr))
 
 
 def _ptr(t) -> int:

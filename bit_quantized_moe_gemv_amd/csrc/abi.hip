@@ -1,5 +1,6 @@
 // abi.hip -- the exported C entry points of libbqmoe.so: argument validation,
 // workspace carving and the launch sequence of one forward pass.
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -270,6 +271,56 @@ int moe_layer_forward(moe_layer *L, const void *x_bf16, int32_t T, const float *
     L->last_T = T;
     L->last_path = path;
     return MOE_OK;
+}
+
+// ---- moe_forward_noalloc: the workspace in a library-owned device array ----
+// One copy per GPU, allocated by the runtime when the code object is loaded
+// on that GPU and held until the process ends.  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, looked up on the first call on that device.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size must keep 256-byte alignment");
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];  // per device id; null until looked up
+
+// The current device's scratch address, or null if the lookup fails.
+static void *scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+int moe_forward_noalloc(const moe_layer_desc *desc, const void *x_bf16, int32_t T,
+                        const float *router_w, const void *packed_experts, float *out,
+                        void *hip_stream) {
+    Shape s;
+    const int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (T < 1 || T > desc->max_tokens) return MOE_EINVAL;
+    if (!aligned16(x_bf16) || !aligned16(router_w) || !aligned16(packed_experts) ||
+        !aligned16(out))
+        return MOE_EINVAL;
+    const int path = choose_path(s, desc->force_path, T);
+    if (path < 0) return path;
+    // the workspace layout of a handle with max_tokens = T
+    if (workspace_bytes(s, T) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+    void *base = scratch_for_current_device();
+    if (!base) return MOE_EHIP;
+    Workspace ws;
+    carve_workspace(s, T, base, &ws);
+    const hipError_t err = enqueue_forward(nullptr, -1, s, ws, path,
+                                           static_cast<const uint16_t *>(x_bf16), T, router_w,
+                                           static_cast<const uint8_t *>(packed_experts), out,
+                                           static_cast<hipStream_t>(hip_stream));
+    return err == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
 int moe_layer_routing(moe_layer *L, int32_t *topk_idx, float *topk_w, int32_t *counts,

@@ -220,6 +220,29 @@ int moe_layer_replay_stage(moe_layer *layer, int32_t stage, int32_t reps, const 
 int moe_read_probe(const void *buf, size_t bytes, size_t copy_stride, int32_t n_copies,
                    int32_t reps, uint32_t *sink, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * pass of moe_layer_forward with no handle and no caller workspace.  The
+ * workspace is a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES on
+ * each GPU the library runs on, held until the process ends; the first call
+ * on a device looks its address up (with that device current).
+ *   desc   host; validated as by moe_layer_create; max_tokens bounds T and
+ *          force_path/routing apply as for a handle
+ *   other arguments as for moe_layer_forward (device pointers, same layouts
+ *   and alignment; out fully overwritten), enqueued on hip_stream
+ * Returns MOE_EINVAL for a bad descriptor or argument, MOE_EWORKSPACE when
+ * the workspace of T tokens (moe_workspace_size with max_tokens = T) exceeds
+ * the array (at the MiMo shape: up to 72 tokens MXFP4, 70 VQ), MOE_EHIP when the address
+ * lookup or a launch fails.  Makes no allocation of any kind.  All calls on
+ * one GPU share its array, and a call leaves its contents behind (no kernel
+ * reads workspace contents that the same call did not write first): calls
+ * that overlap in time on one GPU -- on different streams or from different
+ * threads -- race and give undefined results, so order them on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int moe_forward_noalloc(const moe_layer_desc *desc, const void *x_bf16, int32_t T,
+                        const float *router_w, const void *packed_experts, float *out,
+                        void *hip_stream);
+
 /* Release the handle (not the workspace).  NULL is a no-op. */
 void moe_layer_destroy(moe_layer *layer);
 

@@ -205,3 +205,24 @@ def test_binding_rejects_mismatched_tensors(lib):
         with pytest.raises(ValueError):
             layer._check_args(args["x"], args["router_w"], args["packed"], args["out"])
     layer._check_args(x, wr, pk, out)  # the matching set passes
+
+
+def test_noalloc_validates_before_any_device_call(lib):
+    """moe_forward_noalloc checks its arguments and the workspace size before
+    it touches a device: with no GPU here, reaching the device would return
+    MOE_EHIP, so these codes show the order.  73 MiMo-shaped tokens need more
+    than the 16 MiB array."""
+    desc = bq.moe_layer_desc(4096, 2048, 256, 8, 80, 1, 0, 0)
+    p = 1 << 20  # aligned, never dereferenced
+    f = lib.moe_forward_noalloc
+    assert bq.workspace_size(4096, 2048, 256, 8, 72) <= bq.MOE_NOALLOC_SCRATCH_BYTES
+    assert bq.workspace_size(4096, 2048, 256, 8, 73) > bq.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(desc), p, 73, p, p, p, None) == bq.MOE_EWORKSPACE
+    assert f(ctypes.byref(desc), p, 0, p, p, p, None) == bq.MOE_EINVAL
+    assert f(ctypes.byref(desc), p, 81, p, p, p, None) == bq.MOE_EINVAL
+    assert f(ctypes.byref(desc), p + 8, 4, p, p, p, None) == bq.MOE_EINVAL
+    assert f(None, p, 4, p, p, p, None) == bq.MOE_EINVAL
+    bad = bq.moe_layer_desc(4096, 2048, 256, 9, 80, 1, 0, 0)
+    assert f(ctypes.byref(bad), p, 4, p, p, p, None) == bq.MOE_EINVAL
+    forced = bq.moe_layer_desc(4096, 2048, 256, 8, 80, 1, bq.MOE_PATH_DECODE, 0)
+    assert f(ctypes.byref(forced), p, 17, p, p, p, None) == bq.MOE_EINVAL
