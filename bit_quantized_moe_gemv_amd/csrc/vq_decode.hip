@@ -17,6 +17,10 @@
 // an exact power of two, as in the large-batch kernels.  (At one token the
 // matrix core would waste 15 of its 16 columns.)
 //
+// Every barrier in these kernels orders LDS only (lds_barrier): a full
+// __syncthreads() would also wait for every global load in flight, i.e. the
+// block's whole index stream, before the first gather.
+//
 // Kernels (one token, k routes):
 //  * vq_dec_gateup: block = 4 (gate, up) row-group pairs of one route (8
 //    groups of 16 rows).  Each wave streams GW groups over TJ tiles of K; the
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     }
     const float wm = wave_max_f32(__uint_as_float(mb));
     if (lane == 0) lds.wmax[wave] = wm;
-    __syncthreads();
+    lds_barrier();
     const int e = __builtin_amdgcn_readfirstlane(lds.expert);
 
     const VqMatrix<RES> m(packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes, (size_t)2 * I,
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(lds.x16) + piece_elem(8 * tid))[0] =
             make_uint4(o[0], o[1], o[2], o[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     float acc[GW][2];
 #pragma unroll
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         const float v = row_sum(acc[g]);
         if (q == 0 && wave < NWA) lds.red[js][gset * GW + g][n] = v;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 16 * kVdPairs) {
         const int pr = tid >> 4, r = tid & 15;
         float gs = lds.red[0][2 * pr][r], us = lds.red[0][2 * pr + 1][r];
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     }
 
     store_books<kVdThreads, RES>(lds.bk, tid, bv);
-    __syncthreads();
+    lds_barrier();
     // per-route exponents from the largest |h| (non-negative floats order as
     // their bit patterns)
 #pragma unroll
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
         const float mx = wave_max_f32(a);
         if (lane == 0) atomicMax(&lds.rmax[4 * hh + k], __float_as_uint(mx));
     }
-    __syncthreads();
+    lds_barrier();
     int hs[2][4];
 #pragma unroll
     for (int r = 0; r < 8; ++r) hs[r >> 2][r & 3] = fp16_row_exponent(lds.rmax[r]);
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     float acc[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        if (f > 0) __syncthreads();  // phase 0's readers are done with h16
+        if (f > 0) lds_barrier();  // phase 0's readers are done with h16
         if (hh == f) {
             const int pe = piece_elem(4 * cg);
 #pragma unroll
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
                                    ((uint32_t)__builtin_bit_cast(uint16_t, d) << 16));
             }
         }
-        __syncthreads();
+        lds_barrier();
         float a1[1][2] = {{0.f, 0.f}};
 #pragma unroll
         for (int u = 0; u < TJ; ++u)
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
         const float c1 = l1 ? acc[1] * f16_bits_to_f32(gn[1]) * ldexpf(wgt[1], hs[1][r4]) : 0.f;
         lds.red[wave][n] = c0 + c1;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < 16) {
         float v = lds.red[0][tid];
 #pragma unroll
