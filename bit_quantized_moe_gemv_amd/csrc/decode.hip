@@ -70,7 +70,7 @@ __device__ __forceinline__ void reg_fence(uint4 &v) {
 // products being four times the work per byte.
 // ---------------------------------------------------------------------------
 // With R1 (a single token) the blocks route the token themselves, which
-// replaces a separate routing launch: wave 0 of every streaming block finds the
+// replaces a separate routing launch: every wave of a streaming block finds the
 // selected set of experts (wave_topk_set: ballots only, no ordering or
 // weights) and takes the slot-th selected expert in ascending order; one block
 // of an extra row runs the full ordered selection with its weights (the same
@@ -104,16 +104,13 @@ __global__ __launch_bounds__(128 * KW) void decode_gateup_mxfp4(
             }
             return;
         }
-        __shared__ int s_e;
-        if (threadIdx.x < 64) {  // which expert: only the selected set is needed here
-            float lv[4];
-            topk_load(logits, E, lv);
-            uint64_t m[4];
-            wave_topk_set(lv, E, K, m);
-            if (threadIdx.x == 0) s_e = topk_set_nth(m, slot);
-        }
-        lds_barrier();
-        e = s_e;
+        // which expert: every wave finds it itself (the selected set only,
+        // ballots), so no wave waits on a barrier before its weight stream
+        float lv[4];
+        topk_load(logits, E, lv);
+        uint64_t m[4];
+        wave_topk_set(lv, E, K, m);
+        e = __builtin_amdgcn_readfirstlane(topk_set_nth(m, slot));
         p0 = slot;
         ne = 1;
     } else {
