@@ -5,15 +5,17 @@
 // The micro-batch matters (a 512-token micro-batch leaves much of prefill
 // unused because each of the 256 experts then sees too few tokens per matmul
 // -- TrevorJS GGUF card, "Speed"): a block owns one slice of one expert's
-// weights and multiplies it with the expert's tokens, 64 at a time.
+// weights and multiplies it with all of the expert's tokens, up to 128 of them
+// per pass over the slice, so the slice leaves HBM once.
 //
-// Shape of a kernel: blocks of four waves with 4 row groups (16 weight rows
-// each) per wave, at most 256 registers and 51 KiB of LDS per block,
-// so two independent blocks share each CU and every SIMD runs two waves that
-// hide each other's memory and barrier stalls.  Per K step of 128 columns each
-// wave issues, in a fixed order, its copies of the B stage and of its groups'
-// scales (global_load_lds into an LDS ring) and its 4 code loads (1 KiB wave
-// loads into a register ring), a fixed number of steps ahead.  Loads are
+// Shape of a kernel: one block of eight waves per CU, at most 256 registers
+// per wave and 102 KiB of LDS.  Waves w and w+4 own the same 4 row groups
+// (16 weight rows each) and split the chunk's 16-token tiles evenly between
+// them, so every SIMD runs two waves with the same weights and different
+// tokens (their duplicate code loads are served on chip).  Per K step of 128
+// columns each wave issues, in a fixed order, its copies of the B stage and of
+// its groups' scales (global_load_lds into an LDS ring) and its 4 code loads
+// (1 KiB wave loads into a register ring), a fixed number of steps ahead.  Loads are
 // issued unconditionally (past the end they repeat the last step's
 // addresses) so the wait counts are compile-time constants that the compiler
 // tracks exactly; a conditional issue makes it wait for every load in flight.
@@ -111,38 +113,28 @@ __device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
     return d > 0 ? __uint_as_float((uint32_t)d << 23) : 0.f;
 }
 
-// Token chunks of block half th of an expert with ne tokens: chunk i of the
-// expert (64 tokens) belongs to half i%2.  For 64 < ne <= 128 the two halves
-// take an even split in 16-token tiles instead (the first half gets the odd
-// tile), so the sibling blocks that stream the same weight slice run at the
-// same pace and the second one finds the slice in L2.
-struct ChunkPlan {
-    int c0, nt0;  // first chunk's start and size (nt0 < 0: 64-token chunks throughout)
-};
-__device__ __forceinline__ ChunkPlan chunk_plan(int ne, int th) {
-    if (ne > 64 && ne <= 128) {
-        const int split = 16 * (((ne + 15) / 16 + 1) / 2);
-        return {th ? split : 0, th ? ne - split : split};
-    }
-    return {64 * th, -1};
+// Token tiles of wave half hf (waves 0-3: 0, 4-7: 1) in a chunk of mt 16-token
+// tiles: the first half takes the first ceil(mt/2), the second the rest.
+__device__ __forceinline__ void half_tiles(int mt, int hf, int *tb, int *mtw) {
+    const int mt0 = (mt + 1) >> 1;
+    *tb = hf ? mt0 : 0;
+    *mtw = hf ? mt - mt0 : mt0;
 }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Grid: E * I/128 * 2 blocks of 4 waves; two blocks share
-// a CU (51 KiB of LDS and at most 256 registers per wave each), so every SIMD
-// runs two independent waves that hide each other's stalls.  Block (b, half
-// th) of expert e owns gate row groups 8b..8b+7 and their up partners and the
-// expert's tokens in 64-token chunks th, th+2, ...; wave w computes gate
-// groups 8b+2w, +1 and their up partners.  The two halves of a slice are
-// neighbouring blocks on one XCD, so the second one's weights mostly come
-// from that XCD's L2.  Per 128-column step every wave issues its four 1 KiB
-// pieces of the B stage, the scales of its 4 groups, then its 4 code loads,
-// kGuRing-1 steps ahead, branch-free so the wait counts stay exact.
+// gate/up + SwiGLU.  Grid: E * I/128 blocks of 8 waves, one per CU.  Block b
+// of expert e owns gate row groups 8b..8b+7 and their up partners and all of
+// the expert's tokens, 128 per pass; waves w and w+4 compute gate groups
+// 8b+2(w%4), +1 and their up partners, for the first and the second half of
+// the pass's 16-token tiles.  Per 128-column step every wave issues its four
+// 1 KiB pieces of the B stage, the scales of its 4 groups, then its 4 code
+// loads, kGuRing-1 steps ahead, branch-free so the wait counts stay exact.
 // ---------------------------------------------------------------------------
-constexpr int kGuWaves = 4;
+constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * 64;
-constexpr int kGuGroups = 4;  // row groups per wave
+constexpr int kGuGroups = 4;   // row groups per wave
 constexpr int kGuRing = 3;
+constexpr int kGuChunk = 128;  // tokens per pass over the weight slice (8 tiles)
 
 // B stage of one 128-column step: [chunk group cg][token m][4 x 16 B], the
 // 16-byte chunk c = 4cg + p (columns 8c..8c+7) of token m kept at position
@@ -153,11 +145,12 @@ constexpr int kGuRing = 3;
 // [group][tile q][row] (lane l moves rows 4(l%4)..+3 of tile (l/4)%4 of group
 // l/16), so every wave issues the same loads per step.
 struct GuLds {
-    uint8_t b[kGuRing][4][64][64];          // 16 KiB per slot
-    uint8_t sc[kGuRing][kGuWaves][256];     // 1 KiB per slot
+    uint8_t b[kGuRing][4][kGuChunk][64];    // 32 KiB per slot
+    uint8_t sc[kGuRing][kGuWaves][256];     // 2 KiB per slot
 };
 
-// MFMAs of one step for one wave: 4 K steps x 4 groups x MT token tiles.  MT
+// MFMAs of one step for one wave: 4 K steps x 4 groups x MT token tiles
+// (tiles tb..tb+MT-1 of the chunk).  MT
 // is a template parameter (the chunk's tile count, dispatched once per
 // chunk): with a run-time count every tile's MFMAs sat in a basic block of
 // their own, and the compiler could not interleave them with the next K
@@ -168,7 +161,7 @@ struct GuLds {
 // F16: fp16 operands, the weights scaled relative to the group exponents b[g].
 template <bool F16, int MT>
 __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const GuLds &lds,
-                                        int slot, int wave, int lane,
+                                        int slot, int wave, int lane, int tb,
                                         const int (&b)[kGuGroups], f32x4 (&acc)[kGuGroups][4]) {
     using V8 = std::conditional_t<F16, f16x8, bf16x8>;
     const int q = lane >> 4, n = lane & 15;
@@ -180,11 +173,12 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
     }
     V8 a[2][kGuGroups];
     V8 bv[2][4];
-    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks
+    auto load_b = [&](int buf, int ks) {  // token 16(tb + t) + n, chunk 4q + ks
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            bv[buf][t] = *reinterpret_cast<const V8 *>(
-                &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
+            if (t < MT)
+                bv[buf][t] = *reinterpret_cast<const V8 *>(
+                    &lds.b[slot][q][16 * (tb + t) + n][16 * (ks ^ ((n >> 2) & 3))]);
     };
     auto dequant = [&](int buf, int ks) {
 #pragma unroll
@@ -228,7 +222,7 @@ template <bool F16, int MT>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
                                             int nsuper, const int (&grp)[kGuGroups],
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
-                                            f32x4 (&acc)[kGuGroups][4],
+                                            int tb, f32x4 (&acc)[kGuGroups][4],
                                             int (&b)[kGuGroups]) {
     constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
     uint4 ring[kGuRing][kGuGroups];
@@ -286,37 +280,37 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
             wait_vmcnt<(kGuRing - 2) * C>();  // step J has landed
             stage_barrier();
             issue((jj + kGuRing - 1) % kGuRing, min(J + kGuRing - 1, last));
-            if (J < nsuper) gu_step<F16, MT>(ring[jj], lds, jj, wave, lane, b, acc);
+            if (J < nsuper) gu_step<F16, MT>(ring[jj], lds, jj, wave, lane, tb, b, acc);
         }
     }
     wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
 }
 
-__global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
+__global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes,
     int H, int I, int K, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, float *__restrict__ h) {
     __shared__ __align__(16) GuLds lds;
-    int e, part;
-    map_expert_block(blockIdx.x, E, (I / 128) * 2, &e, &part);
-    const int b = part >> 1, th = part & 1;
+    int e, b;
+    map_expert_block(blockIdx.x, E, I / 128, &e, &b);
     const int p0 = offsets[e];
     const int ne = offsets[e + 1] - p0;
-    if (64 * th >= ne) return;
+    if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave & 3, hf = wave >> 2;  // row-group set, token half
     const int n = lane & 15, q = lane >> 4;
     const int ngate = I / 16;
     const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const size_t kt = (size_t)(H / 32);
     int grp[kGuGroups];
 #pragma unroll
-    for (int g = 0; g < kGuGroups; ++g) grp[g] = (g < 2 ? 0 : ngate) + 8 * b + 2 * wave + (g & 1);
+    for (int g = 0; g < kGuGroups; ++g) grp[g] = (g < 2 ? 0 : ngate) + 8 * b + 2 * wg + (g & 1);
 
-    const ChunkPlan plan = chunk_plan(ne, th);
-    for (int c0 = plan.c0; c0 < ne; c0 += 128) {
-        const int nt = plan.nt0 >= 0 ? plan.nt0 : min(64, ne - c0);
-        const int mt = (nt + 15) / 16;
+    for (int c0 = 0; c0 < ne; c0 += kGuChunk) {
+        const int nt = min(kGuChunk, ne - c0);
+        int tb, mtw;
+        half_tiles((nt + 15) / 16, hf, &tb, &mtw);
         // the token row this lane copies: token 16w + l/4 of the chunk
         const uint16_t *brow =
             x + (size_t)(perm[p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)] / K) * H;
@@ -325,28 +319,29 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > plan.c0) stage_barrier();  // previous chunk's readers are done with the rings
+        if (c0 > 0) stage_barrier();  // previous chunk's readers are done with the rings
         int unused[kGuGroups];
         auto run = [&](auto mtc) {
             gu_pipeline<false, decltype(mtc)::value>(ex, ex + (size_t)I * H, kt, H / 128, grp, lds,
-                                                     brow, wave, lane, acc, unused);
+                                                     brow, wave, lane, tb, acc, unused);
         };
-        switch (mt) {
+        switch (mtw) {
+            case 0: run(std::integral_constant<int, 0>{}); break;
             case 1: run(std::integral_constant<int, 1>{}); break;
             case 2: run(std::integral_constant<int, 2>{}); break;
             case 3: run(std::integral_constant<int, 3>{}); break;
             default: run(std::integral_constant<int, 4>{}); break;
         }
-        // epilogue: lane holds rows 4q..4q+3 of each group for token 16t + n;
+        // epilogue: lane holds rows 4q..4q+3 of each group for token 16(tb+t) + n;
         // gate group i pairs with up group 2 + i
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int m = 16 * t + n;
-            if (m < nt) {
+            const int m = 16 * (tb + t) + n;
+            if (t < mtw && m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const int gg = 8 * b + 2 * wave + i;  // gate group
+                    const int gg = 8 * b + 2 * wg + i;  // gate group
                     float hv[4];
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj)
@@ -360,49 +355,50 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_gateup_mxfp4(
 }
 
 // ---------------------------------------------------------------------------
-// down.  Grid: E * H/256 * 2 blocks of 4 waves, two blocks per CU as in
-// gate/up, on the same pipeline with fp16 operands.  Block (b, half th) owns
-// output row groups 16b..16b+15 (wave w: 16b+4w..+3) and the expert's tokens
-// in 64-token chunks th, th+2, ...; the h16 rows are contiguous (route-position
-// order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
+// down.  Grid: E * H/256 blocks of 8 waves, one per CU, on the same pipeline
+// with fp16 operands.  Block b owns output row groups 16b..16b+15 (waves w
+// and w+4: 16b+4(w%4)..+3, the two halves of each pass's token tiles) and all
+// of the expert's tokens, 128 per pass; the h16 rows are contiguous
+// (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
+__global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
     const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h16,
     const int32_t *__restrict__ hexp, float *__restrict__ y) {
     __shared__ __align__(16) GuLds lds;
-    int e, part;
-    map_expert_block(blockIdx.x, E, (H / 256) * 2, &e, &part);
-    const int b = part >> 1, th = part & 1;
+    int e, b;
+    map_expert_block(blockIdx.x, E, H / 256, &e, &b);
     const int p0 = offsets[e];
     const int ne = offsets[e + 1] - p0;
-    if (64 * th >= ne) return;
+    if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave & 3, hf = wave >> 2;
     const int n = lane & 15, q = lane >> 4;
     const uint8_t *codes = packed + (size_t)e * expert_bytes + (size_t)I * H + (size_t)I * H / 16;
     const size_t kt = (size_t)(I / 32);
     int grp[kGuGroups];
 #pragma unroll
-    for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wave + g;
+    for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wg + g;
 
-    const ChunkPlan plan = chunk_plan(ne, th);
-    for (int c0 = plan.c0; c0 < ne; c0 += 128) {
-        const int nt = plan.nt0 >= 0 ? plan.nt0 : min(64, ne - c0);
-        const int mt = (nt + 15) / 16;
+    for (int c0 = 0; c0 < ne; c0 += kGuChunk) {
+        const int nt = min(kGuChunk, ne - c0);
+        int tb, mtw;
+        half_tiles((nt + 15) / 16, hf, &tb, &mtw);
         const uint16_t *brow = h16 + (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
         f32x4 acc[kGuGroups][4];
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > plan.c0) stage_barrier();
+        if (c0 > 0) stage_barrier();
         int bexp[kGuGroups];
         auto run = [&](auto mtc) {
             gu_pipeline<true, decltype(mtc)::value>(codes, codes + (size_t)H * I / 2, kt, I / 128,
-                                                    grp, lds, brow, wave, lane, acc, bexp);
+                                                    grp, lds, brow, wave, lane, tb, acc, bexp);
         };
-        switch (mt) {
+        switch (mtw) {
+            case 0: run(std::integral_constant<int, 0>{}); break;
             case 1: run(std::integral_constant<int, 1>{}); break;
             case 2: run(std::integral_constant<int, 2>{}); break;
             case 3: run(std::integral_constant<int, 3>{}); break;
@@ -410,11 +406,11 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
         }
         int hs[4];  // row exponents of the lane's tokens, fetched together
 #pragma unroll
-        for (int t = 0; t < 4; ++t) hs[t] = hexp[p0 + c0 + min(16 * t + n, nt - 1)] - 127;
+        for (int t = 0; t < 4; ++t) hs[t] = hexp[p0 + c0 + min(16 * (tb + t) + n, nt - 1)] - 127;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int m = 16 * t + n;
-            if (m < nt) {
+            const int m = 16 * (tb + t) + n;
+            if (t < mtw && m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
                 for (int g = 0; g < kGuGroups; ++g) {
@@ -430,7 +426,7 @@ __global__ __launch_bounds__(kGuThreads, 2) void prefill_down_mxfp4(
 
 hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                  const Workspace &ws, hipStream_t st) {
-    prefill_gateup_mxfp4<<<s.E * (s.I / 128) * 2, kGuThreads, 0, st>>>(
+    prefill_gateup_mxfp4<<<s.E * (s.I / 128), kGuThreads, 0, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm,
         static_cast<float *>(ws.h));
     return hipGetLastError();
@@ -440,7 +436,7 @@ hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, con
                                hipStream_t st) {
     hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
-    prefill_down_mxfp4<<<s.E * (s.H / 256) * 2, kGuThreads, 0, st>>>(
+    prefill_down_mxfp4<<<s.E * (s.H / 256), kGuThreads, 0, st>>>(
         packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, ws.h16, ws.hexp, ws.y);
     return hipGetLastError();
 }
