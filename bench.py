@@ -372,7 +372,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode only")
     ap.add_argument("--only", choices=["decode", "verify", "prefill", "vq_prefill", "vq_decode",
-                                       "copy"],
+                                       "vq13_decode", "vq_verify", "copy"],
                     default=None,
                     help="run one workload without the report (for profilers)")
     ap.add_argument("--no-peaks", action="store_true")
@@ -410,9 +410,14 @@ def main():
     if args.only:
         wl = {"decode": W.DECODE, "verify": W.VERIFY, "prefill": W.PREFILL,
               "vq_prefill": W.VQ_PREFILL,
-              "vq_decode": W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1")}[args.only]
-        res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False,
-                    layers=b.vq_layers() if wl.fmt == W_FMT_VQ else None, replay=args.replay)
+              "vq_decode": W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1"),
+              "vq13_decode": W.VQ13_DECODE,
+              "vq_verify": W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed"),
+              }[args.only]
+        layers = (b.vq_layers() if wl.fmt == W_FMT_VQ else
+                  b.vq13_layers() if wl.fmt == W_FMT_VQ13 else None)
+        res = b.run(wl, args.steps, args.warmup, wl.tokens, profile=False, layers=layers,
+                    replay=args.replay)
         log(json.dumps(res))
         return
 

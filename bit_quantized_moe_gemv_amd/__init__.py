@@ -14,7 +14,8 @@ import os
 from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbqmoe.so")
+# BQMOE_LIBRARY points the binding at another build of the same library
+LIB_PATH = os.environ.get("BQMOE_LIBRARY") or os.path.join(_PKG, "libbqmoe.so")
 
 MOE_OK = 0
 MOE_EINVAL = -1
