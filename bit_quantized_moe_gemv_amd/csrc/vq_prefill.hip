@@ -34,6 +34,8 @@
 // (0..7) of the super-step uses its vector s, i.e. columns 64q+8s..+7.  The B
 // operand of lane (m, q) at K step s is therefore x[m][256J+64q+8s..+7];
 // sub-step u holds K steps 2u and 2u+1.
+#include <type_traits>
+
 #include "vq_common.h"
 
 namespace bqmoe {
@@ -411,6 +413,255 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The grouped GEMM for batches of more than 16 tokens.  Item = (expert,
+// slice); a block covers 256 weight rows of its slice (wave w: row groups
+// grp[0], grp[1]) for all of the expert's tokens, 128 per pass, so each
+// gathered A fragment feeds up to 8 token tiles and an expert of up to 128
+// tokens gathers its weights once.  MODE 0: slice = 128 gate rows and their
+// up partners (wave w: gate group 8*slice + w and its up partner), B = x16
+// gathered through perm, out = h; MODE 1: slice = 256 output rows (wave w:
+// groups 16*slice + 2w, +1), B = h16 (route rows), out = y.  MT: the pass's
+// 16-token tiles, rounded up to even (a compile-time count, dispatched per
+// pass).  B goes through a 3-deep LDS ring of single K steps (4 pieces of 8
+// columns x 128 tokens, 8 KiB); with both books that fills 156 KiB.
+// ---------------------------------------------------------------------------
+constexpr int kVgGroups = 2;
+constexpr int kVgChunk = 128;
+constexpr int kVgRing = 3;
+
+struct VgLds {
+    uint4 cb[kVqEntries];                  // 128 KiB
+    uint4 rb[kVqResEntries];               // 4 KiB
+    uint4 b[kVgRing][4][kVgChunk];         // [slot][q][token]: 8 columns of fp16
+};
+
+// One K step S (0..7 of a 256-column super-step) of a wave: 2 groups x MT
+// token tiles.
+template <int S, int MT, bool RES>
+__device__ __forceinline__ void vg_kstep(const uint32_t (&cr)[kVgGroups][6], const VgLds &lds,
+                                         int slot, int lane, f32x4 (&acc)[kVgGroups][MT]) {
+    const int q = lane >> 4, n = lane & 15;
+    uint4 cbv[kVgGroups], rbv[kVgGroups];
+#pragma unroll
+    for (int g = 0; g < kVgGroups; ++g) {
+        uint32_t i13, i8;
+        vq_indices<S>(cr[g], i13, i8);
+        cbv[g] = lds.cb[i13];
+        if (RES) rbv[g] = lds.rb[i8];
+    }
+    uint4 bv[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) bv[t] = lds.b[slot][q][16 * t + n];
+    f16x8 a[kVgGroups];
+#pragma unroll
+    for (int g = 0; g < kVgGroups; ++g)
+        a[g] = RES ? add_f16x8(cbv[g], rbv[g]) : __builtin_bit_cast(f16x8, cbv[g]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int g = 0; g < kVgGroups; ++g)
+            acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], __builtin_bit_cast(f16x8, bv[t]),
+                                                               acc[g][t], 0, 0, 0);
+}
+
+// One pass (at most 128 tokens from route position pc) over the item's rows.
+template <int MODE, int MT, bool RES>
+__device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const uint8_t *pln,
+                                        const uint8_t *res, const uint16_t *gain,
+                                        const int (&grp)[kVgGroups], int NJ, int H, int I, int K,
+                                        int pc, int nt, int wave, int lane,
+                                        const int32_t *__restrict__ perm,
+                                        const uint16_t *__restrict__ bsrc,
+                                        const int32_t *__restrict__ bexp,
+                                        float *__restrict__ out) {
+    const int q = lane >> 4, n = lane & 15;
+    // B staging: wave w moves piece q = w%4 (columns 64q + 8s..+7 of K step
+    // s) of tokens 64(w/4) + lane, one 16-byte register load per K step
+    const int sq = wave & 3;
+    const int tok = min(64 * (wave >> 2) + lane, nt - 1);
+    const uint16_t *brow = MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H
+                                     : bsrc + (size_t)(pc + tok) * I;
+    f32x4 acc[kVgGroups][MT];
+#pragma unroll
+    for (int g = 0; g < kVgGroups; ++g)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t cr[2][kVgGroups][6];
+    auto issue_codes = [&](int slot, int J) {
+#pragma unroll
+        for (int g = 0; g < kVgGroups; ++g) {
+            const size_t tile = (size_t)grp[g] * NJ + J;
+            const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
+            uint2 r = make_uint2(0u, 0u);
+            if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
+            const uint32_t p = pln[tile * 64 + lane];
+            cr[slot][g][0] = c.x;
+            cr[slot][g][1] = c.y;
+            cr[slot][g][2] = c.z;
+            cr[slot][g][3] = r.x;
+            cr[slot][g][4] = r.y;
+            cr[slot][g][5] = p;
+        }
+    };
+    uint4 bstage;
+    auto load_b = [&](int S) {  // K step S = 8J + s
+        bstage = *reinterpret_cast<const uint4 *>(brow + 256 * (S >> 3) + 64 * sq + 8 * (S & 7));
+    };
+    auto store_b = [&](int S) { lds.b[S % kVgRing][sq][64 * (wave >> 2) + lane] = bstage; };
+    constexpr int kCodeLoads = (RES ? 3 : 2) * kVgGroups;
+
+    vq_stage_barrier();  // the previous pass's readers are done with the ring
+    const int NS = 8 * NJ, lastS = NS - 1, lastJ = NJ - 1;
+    issue_codes(0, 0);
+    load_b(0);
+    vq_wait_vmcnt<0>();
+    store_b(0);
+    load_b(min(1, lastS));
+    // Per K step S = 8J+s: B(S+1) (issued at S-1, followed by the code loads
+    // of super-step J when S-1 began one) lands and goes to LDS; the barrier
+    // publishes B(S); then B(S+2) and, at s = 0, the codes of super-step J+1
+    // are issued.  Loads are issued every step (indices clamped past the
+    // end), so the wait counts are exact.
+    for (int J0 = 0; J0 < NJ; J0 += 2) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int J = J0 + jj;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int S = 8 * J + s;
+                if (s == 1)
+                    vq_wait_vmcnt<kCodeLoads>();
+                else
+                    vq_wait_vmcnt<0>();
+                store_b(min(S + 1, lastS));
+                vq_stage_barrier();
+                load_b(min(S + 2, lastS));
+                if (s == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
+                if (J < NJ) {
+                    const int slot = S % kVgRing;
+                    if (s == 0) vg_kstep<0, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 1) vg_kstep<1, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 2) vg_kstep<2, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 3) vg_kstep<3, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 4) vg_kstep<4, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 5) vg_kstep<5, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 6) vg_kstep<6, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 7) vg_kstep<7, MT, RES>(cr[jj], lds, slot, lane, acc);
+                }
+            }
+        }
+    }
+    vq_wait_vmcnt<0>();  // the repeated tail loads land before the ring is reused
+
+    // epilogue: lane holds rows 4q..4q+3 of each group for token 16t+n
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + n;
+        if (m >= nt) continue;
+        const int p = pc + m;
+        if (MODE == 0) {
+            const int xs = bexp[perm[p] / K];
+            const int gg = grp[0], ug = grp[1];
+            const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
+            const uint2 uw = *reinterpret_cast<const uint2 *>(gain + 16 * ug + 4 * q);
+            const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
+            const uint32_t ub[4] = {uw.x & 0xFFFFu, uw.x >> 16, uw.y & 0xFFFFu, uw.y >> 16};
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float gv = ldexpf(acc[0][t][j] * f16_bits_to_f32(gb[j]), xs);
+                const float uv = ldexpf(acc[1][t][j] * f16_bits_to_f32(ub[j]), xs);
+                hv[j] = silu_f32(gv) * uv;
+            }
+            *reinterpret_cast<float4 *>(out + (size_t)p * I + 16 * gg + 4 * q) =
+                make_float4(hv[0], hv[1], hv[2], hv[3]);
+        } else {
+            const int hs = bexp[p];
+#pragma unroll
+            for (int g = 0; g < kVgGroups; ++g) {
+                const int gg = grp[g];
+                if (gg >= H / 16) continue;  // clamped duplicate past the last group
+                if (g == 1 && grp[1] == grp[0]) continue;
+                const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
+                const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
+                float yv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) yv[j] = ldexpf(acc[g][t][j] * f16_bits_to_f32(gb[j]), hs);
+                *reinterpret_cast<float4 *>(out + (size_t)p * H + 16 * gg + 4 * q) =
+                    make_float4(yv[0], yv[1], yv[2], yv[3]);
+            }
+        }
+    }
+}
+
+template <int MODE, bool RES>
+__global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
+    const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int E,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const uint16_t *__restrict__ bsrc, const int32_t *__restrict__ bexp,
+    float *__restrict__ out) {
+    __shared__ __align__(16) VgLds lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    {  // both books -> LDS, once per block
+        const uint4 *books = reinterpret_cast<const uint4 *>(packed);
+        for (int i = tid; i < kVqEntries; i += kVqThreads) lds.cb[i] = books[i];
+        if (RES)
+            for (int i = tid; i < kVqResEntries; i += kVqThreads) lds.rb[i] = books[kVqEntries + i];
+    }
+    __syncthreads();
+
+    const int NK = MODE == 0 ? H : I;        // reduction length
+    const int NROW = MODE == 0 ? 2 * I : H;  // matrix rows
+    const int NJ = NK / 256;                 // super-steps
+    const int nslice = MODE == 0 ? I / 128 : (H + 255) / 256;
+    const size_t nvec = (size_t)NROW * NK / 8;
+    const size_t mat_off = MODE == 1 ? vq_down_offset((size_t)H, (size_t)I, RES) : 0;
+    // blockIdx -> items: with E and the grid multiples of 8, the blocks of one
+    // XCD take the experts e = xcd (mod 8), so an expert's rows stay in one L2
+    const bool by_xcd = (E & 7) == 0 && (gridDim.x & 7) == 0;
+    const int xcd = by_xcd ? (int)(blockIdx.x & 7) : 0;
+    const int first = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    const int stride = by_xcd ? (int)(gridDim.x >> 3) : (int)gridDim.x;
+    const int items = by_xcd ? (E >> 3) * nslice : E * nslice;
+
+    for (int it = first; it < items; it += stride) {
+        const int e = by_xcd ? xcd + 8 * (it / nslice) : it / nslice;
+        const int slice = it % nslice;
+        const int p0 = offsets[e];
+        const int ne = offsets[e + 1] - p0;
+        if (ne == 0) continue;
+        const uint8_t *mat = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
+        const uint8_t *c12 = mat;
+        const uint8_t *pln = c12 + nvec * 3 / 2;
+        const uint8_t *res = pln + nvec / 8;
+        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
+        int grp[kVgGroups];
+        if (MODE == 0) {
+            grp[0] = 8 * slice + wave;          // gate group
+            grp[1] = I / 16 + 8 * slice + wave;  // its up partner
+        } else {
+            grp[0] = min(16 * slice + 2 * wave, H / 16 - 1);
+            grp[1] = min(16 * slice + 2 * wave + 1, H / 16 - 1);
+        }
+        for (int c0 = 0; c0 < ne; c0 += kVgChunk) {
+            const int nt = min(kVgChunk, ne - c0);
+            const int mt = (nt + 15) / 16;
+            auto pass = [&](auto mtc) {
+                vg_pass<MODE, decltype(mtc)::value, RES>(lds, c12, pln, res, gain, grp, NJ, H, I,
+                                                         K, p0 + c0, nt, wave, lane, perm, bsrc,
+                                                         bexp, out);
+            };
+            if (mt <= 2) pass(std::integral_constant<int, 2>{});
+            else if (mt <= 4) pass(std::integral_constant<int, 4>{});
+            else if (mt <= 6) pass(std::integral_constant<int, 6>{});
+            else pass(std::integral_constant<int, 8>{});
+        }
+    }
+}
+
 // Persistent grid: one block per CU (the books fill most of the LDS), a
 // multiple of 8 when there is enough work so every XCD gets the same share.
 static int vq_grid(int items) {
@@ -425,6 +676,19 @@ static void vq_launch3(const Shape &s, int items, const uint8_t *packed, const W
     vq_prefill_kernel<MODE, NTT, RES><<<vq_grid(items), kVqThreads, 0, st>>>(
         packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.active, bsrc, bexp,
         out);
+}
+
+template <int MODE>
+static void vg_launch(const Shape &s, const uint8_t *packed, const Workspace &ws,
+                      const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
+    const int nslice = MODE == 0 ? s.I / 128 : (s.H + 255) / 256;
+    const int grid = vq_grid(s.E * nslice);
+    if (s.fmt == MOE_FMT_VQ13R8)
+        vq_grouped_kernel<MODE, true><<<grid, kVqThreads, 0, st>>>(
+            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out);
+    else
+        vq_grouped_kernel<MODE, false><<<grid, kVqThreads, 0, st>>>(
+            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out);
 }
 
 template <int MODE, int NTT>
@@ -461,7 +725,7 @@ hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
     if (T <= kDecodeMaxTokens)
         vq_launch<0, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.x16, ws.xexp, h, st);
     else
-        vq_launch<0, 4>(s, s.E * ns * kVqChunkLanes, packed, ws, ws.x16, ws.xexp, h, st);
+        vg_launch<0>(s, packed, ws, ws.x16, ws.xexp, h, st);
     return hipGetLastError();
 }
 
@@ -473,7 +737,7 @@ hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
     if (T <= kDecodeMaxTokens)
         vq_launch<1, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.h16, ws.hexp, ws.y, st);
     else
-        vq_launch<1, 4>(s, s.E * ns * kVqChunkLanes, packed, ws, ws.h16, ws.hexp, ws.y, st);
+        vg_launch<1>(s, packed, ws, ws.h16, ws.hexp, ws.y, st);
     return hipGetLastError();
 }
 
