@@ -173,6 +173,50 @@ class Bench:
             torch.cuda.synchronize()
         return self._vq13
 
+    def graph_steps(self, wl, n_cap=64, reps=40):
+        """The step replayed from a captured graph: n_cap forwards (a fresh
+        token each, cycling the layer copies) captured once into a graph, the
+        graph replayed reps times between two HIP events; microseconds per
+        forward."""
+        torch, bq, W = self.torch, self.bq, self.W
+        T = wl.tokens
+        x = W.make_x(wl, tokens=T * n_cap, stream_offset=77)
+        xd = torch.from_numpy(x.view("int16")).to("cuda").view(torch.bfloat16).view(n_cap, T,
+                                                                                  wl.hidden)
+        wr = torch.from_numpy(W.make_router(wl)).to("cuda")
+        layer = bq.MoeLayer(wl.hidden, wl.inter, wl.experts, wl.top_k, T, wl.fmt, 0,
+                            routing=wl.routing)
+        out = torch.empty((T, wl.hidden), dtype=torch.float32, device="cuda")
+        _, base, stride, L = self.layers
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm the handle outside the capture
+            layer.forward(xd[0], wr, self.layers[0][:stride], out=out, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = torch.cuda.current_stream().cuda_stream
+            for i in range(n_cap):
+                rc = layer.forward_raw(int(xd[i].data_ptr()), T, int(wr.data_ptr()),
+                                       base + (i % L) * stride, int(out.data_ptr()), st)
+                if rc != 0:
+                    raise bq.MoeError(rc, "moe_layer_forward (capture)")
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n_cap)
+        del g
+        layer.close()
+        return round(us, 3)
+
     def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0,
             path=0):
         torch, bq, W = self.torch, self.bq, self.W
@@ -432,6 +476,8 @@ def main():
             "traffic": _traffic("decode_gateup_mxfp4", ("decode.hip", "moe_internal.h"), 1),
             "algorithmic_bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": gu_us}
     step_gbs = alg["step_bytes"] / (dec["ms_per_step"] * 1e-3) / 1e9
+    log("decode T=1 replayed from a captured graph")
+    dec["graph_us_per_step"] = b.graph_steps(W.DECODE)
     extra = {"decode_t1": {**dec, "step_algorithmic_bytes": alg["step_bytes"],
                            "step_hbm_gbs": round(step_gbs, 1),
                            "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

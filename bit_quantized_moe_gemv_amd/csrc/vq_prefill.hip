@@ -20,20 +20,23 @@
 // fp32 h values round once to fp16 (relative 2^-11).
 //
 // Both books (128 KiB + 4 KiB) live in LDS for the whole kernel: blocks are
-// persistent (one per CU) and loop over (expert, row slice, token chunk)
-// items, so the books are loaded once per CU.  A lane gathers its A operand
-// with two 16-byte LDS reads per K step.  The B operand (64 tokens) streams
-// through a 3-deep LDS ring of 64-column sub-steps (8 KiB each) with
-// global_load_lds; the index streams of a 256-column super-step go straight
-// to registers one super-step ahead.
+// persistent (one per CU) and loop over (expert, row slice) items, so the
+// books are loaded once per CU.  A lane gathers its A operand with two
+// 16-byte LDS reads per K step.  Batches of more than 16 tokens run
+// vq_grouped_kernel: an item covers 256 weight rows and all of the expert's
+// tokens, 128 per pass (up to 8 token tiles per gathered A fragment), with
+// the B operand streaming through a 3-deep LDS ring of single K steps (8
+// KiB each); batches of at most 16 tokens run vq_prefill_kernel over the
+// active experts only, one 16-token tile per MFMA, B in a ring of two-K-step
+// sub-steps.  The index streams of a 256-column super-step go straight to
+// registers one super-step ahead.
 //
 // Lane roles.  A = 16 weight rows x 32 K of fp16 (lane l: row l%16, K slice
 // 8*(l/16)..+7).  In a VQ tile (16 rows x 256 columns) lane (n, q) owns the
 // eight vectors of row n in columns 64q..64q+63 -- 12 contiguous code12 bytes,
 // 8 res bytes and one plane byte at lane-contiguous offsets -- and K step s
 // (0..7) of the super-step uses its vector s, i.e. columns 64q+8s..+7.  The B
-// operand of lane (m, q) at K step s is therefore x[m][256J+64q+8s..+7];
-// sub-step u holds K steps 2u and 2u+1.
+// operand of lane (m, q) at K step s is therefore x[m][256J+64q+8s..+7].
 #include <type_traits>
 
 #include "vq_common.h"
@@ -44,7 +47,6 @@ constexpr int kVqWaves = 8;  // two per SIMD, sharing the books
 constexpr int kVqThreads = kVqWaves * 64;
 constexpr int kVqGroups = 4;  // row groups (16 rows) per wave; 512 rows per block item
 constexpr int kVqRing = 3;    // B sub-stages in LDS
-constexpr int kVqChunkLanes = 2;  // an expert's 64-token chunks are dealt to 2 items
 
 struct VqLds {
     uint4 cb[kVqEntries];     // 128 KiB
@@ -210,17 +212,16 @@ __device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], c
 }
 
 // ---------------------------------------------------------------------------
-// The grouped GEMM.  MODE 0: gate/up + SwiGLU, B = x16 (gathered through
-// perm), out = h (fp32, [route position][I]).  MODE 1: down, B = h16 (route
-// rows), out = y (fp32, [route position][H]).  Item = (expert, slice, chunk
-// lane); MODE 0 slices are 256 gate rows with their up partners (wave w: gate
-// groups 16b+2w, +1 and the two up partners), MODE 1 slices are 512 output
-// rows (wave w: groups 32b+4w..+3, clamped past the end and never stored).
-// NTT = 4: 64-token chunks over all E experts.  NTT = 1 (batches of at most
-// 16 tokens, so at most 16 routes per expert): one 16-token chunk per item,
-// and the items run over the active experts only (the list the small-batch
-// routing writes), so no MFMA works on absent tokens or experts.  RES: the
-// layer has the residual stage (VQ13R8) or not (VQ13).
+// The grouped GEMM for batches of at most 16 tokens (so at most 16 routes per
+// expert).  MODE 0: gate/up + SwiGLU, B = x16 (gathered through perm), out =
+// h (fp32, [route position][I]).  MODE 1: down, B = h16 (route rows), out = y
+// (fp32, [route position][H]).  Item = (active expert, slice): MODE 0 slices
+// are 256 gate rows with their up partners (wave w: gate groups 16b+2w, +1
+// and the two up partners), MODE 1 slices are 512 output rows (wave w: groups
+// 32b+4w..+3, clamped past the end and never stored).  One 16-token tile per
+// MFMA (NTT = 1), and the items run over the active experts only (the list
+// the small-batch routing writes), so no MFMA works on absent tokens or
+// experts.  RES: the layer has the residual stage (VQ13R8) or not (VQ13).
 // ---------------------------------------------------------------------------
 template <int MODE, int NTT, bool RES>
 __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
@@ -228,9 +229,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ active, const uint16_t *__restrict__ bsrc,
     const int32_t *__restrict__ bexp, float *__restrict__ out) {
-    constexpr bool kSmall = NTT == 1;
-    constexpr int kChunk = 16 * NTT;                   // tokens per chunk
-    constexpr int kLanes = kSmall ? 1 : kVqChunkLanes;  // items per (expert, slice)
+    static_assert(NTT == 1, "larger batches run vq_grouped_kernel");
+    constexpr int kChunk = 16;  // tokens per chunk: every routed expert of a small batch
     __shared__ __align__(16) VqLds lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -249,24 +249,18 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
     const int NJ = NK / 256;                 // super-steps
     const int NS = 4 * NJ;                   // sub-steps
     const int nslice = MODE == 0 ? I / 256 : (H + 511) / 512;
-    const int per_e = nslice * kLanes;
+    const int per_e = nslice;
     const size_t nvec = (size_t)NROW * NK / 8;
     const size_t mat_off = MODE == 1 ? vq_down_offset((size_t)H, (size_t)I, RES) : 0;
     constexpr int kCodeLoads = (RES ? 3 : 2) * kVqGroups;  // loads per wave per super-step
 
-    // blockIdx -> items: with E and the grid multiples of 8, the blocks of one
-    // XCD (the dispatcher deals blocks round-robin over the 8 XCDs) take the
-    // experts e = xcd (mod 8), so an expert's token rows stay in one L2.
-    const bool by_xcd = !kSmall && (E & 7) == 0 && (gridDim.x & 7) == 0;
-    const int xcd = by_xcd ? (int)(blockIdx.x & 7) : 0;
-    const int first = by_xcd ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-    const int stride = by_xcd ? (int)(gridDim.x >> 3) : (int)gridDim.x;
-    const int items = kSmall ? active[0] * per_e : by_xcd ? (E >> 3) * per_e : E * per_e;
+    const int first = (int)blockIdx.x, stride = (int)gridDim.x;
+    const int items = active[0] * per_e;  // the active experts only
 
     for (int it = first; it < items; it += stride) {
-        const int e = kSmall ? active[1 + it / per_e] : by_xcd ? xcd + 8 * (it / per_e) : it / per_e;
+        const int e = active[1 + it / per_e];
         const int rest = it % per_e;
-        const int slice = rest / kLanes, chl = rest % kLanes;
+        const int slice = rest;
         const int p0 = offsets[e];
         const int ne = offsets[e + 1] - p0;
         const uint8_t *mat = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
@@ -284,7 +278,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
                 grp[g] = min(32 * slice + 4 * wave + g, H / 16 - 1);
         }
 
-        for (int c0 = kChunk * chl; c0 < ne; c0 += kChunk * kLanes) {
+        for (int c0 = 0; c0 < ne; c0 += kChunk) {
             const int nt = min(kChunk, ne - c0);
             const int pr = p0 + c0 + min(lane, nt - 1);
             const uint16_t *brow =
