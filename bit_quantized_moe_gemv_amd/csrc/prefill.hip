@@ -9,16 +9,16 @@
 // per pass over the slice, so the slice leaves HBM once.
 //
 // Shape of a kernel: one block of eight waves per CU, at most 256 registers
-// per wave and 102 KiB of LDS.  Waves w and w+4 own the same 4 row groups
-// (16 weight rows each) and split the chunk's 16-token tiles evenly between
-// them, so every SIMD runs two waves with the same weights and different
-// tokens (their duplicate code loads are served on chip).  Per K step of 128
-// columns each wave issues, in a fixed order, its copies of the B stage and of
-// its groups' scales (global_load_lds into an LDS ring) and its 4 code loads
-// (1 KiB wave loads into a register ring), a fixed number of steps ahead.  Loads are
-// issued unconditionally (past the end they repeat the last step's
-// addresses) so the wait counts are compile-time constants that the compiler
-// tracks exactly; a conditional issue makes it wait for every load in flight.
+// per wave and 102 KiB of LDS.  Each wave owns 2 row groups (16 weight rows
+// each; for gate/up a gate group and its up partner) and all of the pass's
+// 16-token tiles, so no two waves load or dequantise the same weights.  Per K
+// step of 128 columns each wave issues, in a fixed order, its copies of the B
+// stage and of its groups' scales (global_load_lds into an LDS ring) and its 2
+// code loads (1 KiB wave loads into a register ring), a fixed number of steps
+// ahead.  Loads are issued unconditionally (past the end they repeat the last
+// step's addresses) so the wait counts are compile-time constants that the
+// compiler tracks exactly; a conditional issue makes it wait for every load in
+// flight.
 //
 // Weights are dequantised to bf16 in registers: every E2M1 value times an
 // in-range E8M0 scale is a bf16 value, so the A operand and the products are
@@ -113,56 +113,48 @@ __device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
     return d > 0 ? __uint_as_float((uint32_t)d << 23) : 0.f;
 }
 
-// Token tiles of wave half hf (waves 0-3: 0, 4-7: 1) in a chunk of mt 16-token
-// tiles: the first half takes the first ceil(mt/2), the second the rest.
-__device__ __forceinline__ void half_tiles(int mt, int hf, int *tb, int *mtw) {
-    const int mt0 = (mt + 1) >> 1;
-    *tb = hf ? mt0 : 0;
-    *mtw = hf ? mt - mt0 : mt0;
-}
-
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  Grid: E * I/128 blocks of 8 waves, one per CU.  Block b
 // of expert e owns gate row groups 8b..8b+7 and their up partners and all of
-// the expert's tokens, 128 per pass; waves w and w+4 compute gate groups
-// 8b+2(w%4), +1 and their up partners, for the first and the second half of
-// the pass's 16-token tiles.  Per 128-column step every wave issues its four
-// 1 KiB pieces of the B stage, the scales of its 4 groups, then its 4 code
-// loads, kGuRing-1 steps ahead, branch-free so the wait counts stay exact.
+// the expert's tokens, 128 per pass; wave w computes gate group 8b+w and its
+// up partner for every 16-token tile of the pass.  Per 128-column step every
+// wave issues its four 1 KiB pieces of the B stage, the scales of its 2
+// groups, then its 2 code loads, kGuRing-1 steps ahead, branch-free so the
+// wait counts stay exact.
 // ---------------------------------------------------------------------------
 constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * 64;
-constexpr int kGuGroups = 4;   // row groups per wave
+constexpr int kGuGroups = 2;   // row groups per wave
 constexpr int kGuRing = 3;
-constexpr int kGuChunk = 128;  // tokens per pass over the weight slice (8 tiles)
+constexpr int kGuChunk = 128;  // tokens per pass over the weight slice
+constexpr int kGuTiles = kGuChunk / 16;
 
 // B stage of one 128-column step: [chunk group cg][token m][4 x 16 B], the
 // 16-byte chunk c = 4cg + p (columns 8c..8c+7) of token m kept at position
 // p ^ ((m/4) % 4).  A copy instruction moves 64 contiguous bytes of each of 16
 // token rows (lane l: token 16w + l/4, position l%4), and the MFMA reads of
 // 16 tokens touch 16 distinct bank groups.
-// Scales: each wave copies those of its own 4 groups, 256 B per step laid out
-// [group][tile q][row] (lane l moves rows 4(l%4)..+3 of tile (l/4)%4 of group
-// l/16), so every wave issues the same loads per step.
+// Scales: each wave copies those of its own 2 groups, 128 B per step laid out
+// [group][tile q][row] (lane l < 32 moves rows 4(l%4)..+3 of tile (l/4)%4 of
+// group l/16; lanes 32-63 repeat that into the unused upper half).
 struct GuLds {
     uint8_t b[kGuRing][4][kGuChunk][64];    // 32 KiB per slot
     uint8_t sc[kGuRing][kGuWaves][256];     // 2 KiB per slot
 };
 
-// MFMAs of one step for one wave: 4 K steps x 4 groups x MT token tiles
-// (tiles tb..tb+MT-1 of the chunk).  MT
+// MFMAs of one step for one wave: 4 K steps x 2 groups x MT token tiles.  MT
 // is a template parameter (the chunk's tile count, dispatched once per
 // chunk): with a run-time count every tile's MFMAs sat in a basic block of
 // their own, and the compiler could not interleave them with the next K
-// step's LDS reads and conversions (measured: 7% slower).  The
-// next K step's B operands and dequantised A operands are prepared before the
-// current K step's MFMAs (double buffering).  Every step dequantises, even
-// with no token tile, so no load is left in flight on a ring register.
+// step's LDS reads and conversions.  The next K step's B operands and
+// dequantised A operands are prepared before the current K step's MFMAs
+// (double buffering).
 // F16: fp16 operands, the weights scaled relative to the group exponents b[g].
 template <bool F16, int MT>
 __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const GuLds &lds,
-                                        int slot, int wave, int lane, int tb,
-                                        const int (&b)[kGuGroups], f32x4 (&acc)[kGuGroups][4]) {
+                                        int slot, int wave, int lane,
+                                        const int (&b)[kGuGroups],
+                                        f32x4 (&acc)[kGuGroups][kGuTiles]) {
     using V8 = std::conditional_t<F16, f16x8, bf16x8>;
     const int q = lane >> 4, n = lane & 15;
     float scale[kGuGroups];
@@ -172,13 +164,12 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
         scale[g] = F16 ? e8m0_rel_f32(e, b[g]) : e8m0_to_f32(e);
     }
     V8 a[2][kGuGroups];
-    V8 bv[2][4];
-    auto load_b = [&](int buf, int ks) {  // token 16(tb + t) + n, chunk 4q + ks
+    V8 bv[2][MT];
+    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (t < MT)
-                bv[buf][t] = *reinterpret_cast<const V8 *>(
-                    &lds.b[slot][q][16 * (tb + t) + n][16 * (ks ^ ((n >> 2) & 3))]);
+        for (int t = 0; t < MT; ++t)
+            bv[buf][t] = *reinterpret_cast<const V8 *>(
+                &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
     };
     auto dequant = [&](int buf, int ks) {
 #pragma unroll
@@ -193,8 +184,6 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
     };
     load_b(0, 0);
     dequant(0, 0);
-    // raised issue priority while this wave has MFMAs to issue, so the
-    // co-resident block's waves, busy with loads and barriers, yield to it
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -204,12 +193,10 @@ __device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const Gu
             dequant(cur ^ 1, ks + 1);
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (t < MT) {
+        for (int t = 0; t < MT; ++t)
 #pragma unroll
-                for (int g = 0; g < kGuGroups; ++g)
-                    acc[g][t] = mfma_op(a[cur][g], bv[cur][t], acc[g][t]);
-            }
+            for (int g = 0; g < kGuGroups; ++g)
+                acc[g][t] = mfma_op(a[cur][g], bv[cur][t], acc[g][t]);
     }
     __builtin_amdgcn_s_setprio(0);
 }
@@ -222,13 +209,13 @@ template <bool F16, int MT>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
                                             int nsuper, const int (&grp)[kGuGroups],
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
-                                            int tb, f32x4 (&acc)[kGuGroups][4],
+                                            f32x4 (&acc)[kGuGroups][kGuTiles],
                                             int (&b)[kGuGroups]) {
     constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
     uint4 ring[kGuRing][kGuGroups];
     uint32_t goff[kGuGroups];
     const uint32_t soff =
-        (uint32_t)(((size_t)grp[lane >> 4] * kt + ((lane >> 2) & 3)) * 16) + 4 * (lane & 3);
+        (uint32_t)(((size_t)grp[(lane >> 4) & 1] * kt + ((lane >> 2) & 3)) * 16) + 4 * (lane & 3);
 #pragma unroll
     for (int g = 0; g < kGuGroups; ++g)
         goff[g] = (uint32_t)((size_t)grp[g] * kt * 256) + lane * 16;
@@ -239,7 +226,7 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             copy_lds16(brow + 128 * J + 8 * (4 * i + swz), lds.b[slot][i][16 * wave]);
-        // scales: lane l copies rows 4(l%4)..+3 of tile 4J + (l/4)%4 of group l/16
+        // scales: lane l copies rows 4(l%4)..+3 of tile 4J + (l/4)%4 of group (l/16)%2
         copy_lds4(scales + soff + (size_t)J * 64, lds.sc[slot][wave]);
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
@@ -250,10 +237,9 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
     for (int j = 0; j < kGuRing - 1; ++j) issue(j, min(j, last));
     if constexpr (F16) {
         // b[g] = the largest E8M0 exponent of row group grp[g] (kt tiles of 16
-        // bytes), read while the first steps are in flight
-        // (the four groups' loads of a pass are issued together; past the
-        // last tile lanes repeat it)
-        uint32_t m[kGuGroups] = {0, 0, 0, 0};
+        // bytes), read while the first steps are in flight (past the last
+        // tile lanes repeat it)
+        uint32_t m[kGuGroups] = {0, 0};
         for (size_t c0 = 0; c0 < kt; c0 += 64) {
             const size_t c = min(c0 + (size_t)lane, kt - 1);
             uint4 v[kGuGroups];
@@ -280,10 +266,25 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
             wait_vmcnt<(kGuRing - 2) * C>();  // step J has landed
             stage_barrier();
             issue((jj + kGuRing - 1) % kGuRing, min(J + kGuRing - 1, last));
-            if (J < nsuper) gu_step<F16, MT>(ring[jj], lds, jj, wave, lane, tb, b, acc);
+            if (J < nsuper) gu_step<F16, MT>(ring[jj], lds, jj, wave, lane, b, acc);
         }
     }
     wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
+}
+
+// Runs f(integral_constant<int, mt>) for a tile count mt in 1..kGuTiles.
+template <typename F>
+__device__ __forceinline__ void with_tiles(int mt, F &&f) {
+    switch (mt) {
+        case 1: f(std::integral_constant<int, 1>{}); break;
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 3: f(std::integral_constant<int, 3>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 5: f(std::integral_constant<int, 5>{}); break;
+        case 6: f(std::integral_constant<int, 6>{}); break;
+        case 7: f(std::integral_constant<int, 7>{}); break;
+        default: f(std::integral_constant<int, 8>{}); break;
+    }
 }
 
 __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
@@ -298,57 +299,42 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
     if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = wave & 3, hf = wave >> 2;  // row-group set, token half
     const int n = lane & 15, q = lane >> 4;
     const int ngate = I / 16;
     const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const size_t kt = (size_t)(H / 32);
-    int grp[kGuGroups];
-#pragma unroll
-    for (int g = 0; g < kGuGroups; ++g) grp[g] = (g < 2 ? 0 : ngate) + 8 * b + 2 * wg + (g & 1);
+    const int gg = 8 * b + wave;  // this wave's gate group
+    const int grp[kGuGroups] = {gg, ngate + gg};
 
     for (int c0 = 0; c0 < ne; c0 += kGuChunk) {
         const int nt = min(kGuChunk, ne - c0);
-        int tb, mtw;
-        half_tiles((nt + 15) / 16, hf, &tb, &mtw);
+        const int mt = (nt + 15) / 16;
         // the token row this lane copies: token 16w + l/4 of the chunk
         const uint16_t *brow =
             x + (size_t)(perm[p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)] / K) * H;
-        f32x4 acc[kGuGroups][4];
+        f32x4 acc[kGuGroups][kGuTiles];
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 0) stage_barrier();  // previous chunk's readers are done with the rings
         int unused[kGuGroups];
-        auto run = [&](auto mtc) {
+        with_tiles(mt, [&](auto mtc) {
             gu_pipeline<false, decltype(mtc)::value>(ex, ex + (size_t)I * H, kt, H / 128, grp, lds,
-                                                     brow, wave, lane, tb, acc, unused);
-        };
-        switch (mtw) {
-            case 0: run(std::integral_constant<int, 0>{}); break;
-            case 1: run(std::integral_constant<int, 1>{}); break;
-            case 2: run(std::integral_constant<int, 2>{}); break;
-            case 3: run(std::integral_constant<int, 3>{}); break;
-            default: run(std::integral_constant<int, 4>{}); break;
-        }
-        // epilogue: lane holds rows 4q..4q+3 of each group for token 16(tb+t) + n;
-        // gate group i pairs with up group 2 + i
+                                                     brow, wave, lane, acc, unused);
+        });
+        // epilogue: lane holds rows 4q..4q+3 of the gate group (acc[0]) and of
+        // its up partner (acc[1]) for token 16t + n
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int m = 16 * (tb + t) + n;
-            if (t < mtw && m < nt) {
+        for (int t = 0; t < kGuTiles; ++t) {
+            const int m = 16 * t + n;
+            if (t < mt && m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
+                float hv[4];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int gg = 8 * b + 2 * wg + i;  // gate group
-                    float hv[4];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        hv[jj] = silu_f32(acc[i][t][jj]) * acc[2 + i][t][jj];
-                    *reinterpret_cast<float4 *>(h + p * I + (size_t)16 * gg + 4 * q) =
-                        make_float4(hv[0], hv[1], hv[2], hv[3]);
-                }
+                for (int jj = 0; jj < 4; ++jj) hv[jj] = silu_f32(acc[0][t][jj]) * acc[1][t][jj];
+                *reinterpret_cast<float4 *>(h + p * I + (size_t)16 * gg + 4 * q) =
+                    make_float4(hv[0], hv[1], hv[2], hv[3]);
             }
         }
     }
@@ -356,10 +342,9 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
 
 // ---------------------------------------------------------------------------
 // down.  Grid: E * H/256 blocks of 8 waves, one per CU, on the same pipeline
-// with fp16 operands.  Block b owns output row groups 16b..16b+15 (waves w
-// and w+4: 16b+4(w%4)..+3, the two halves of each pass's token tiles) and all
-// of the expert's tokens, 128 per pass; the h16 rows are contiguous
-// (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
+// with fp16 operands.  Block b owns output row groups 16b..16b+15 (wave w:
+// 16b+2w, +1) and all of the expert's tokens, 128 per pass; the h16 rows are
+// contiguous (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
@@ -373,44 +358,33 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = wave & 3, hf = wave >> 2;
     const int n = lane & 15, q = lane >> 4;
     const uint8_t *codes = packed + (size_t)e * expert_bytes + (size_t)I * H + (size_t)I * H / 16;
     const size_t kt = (size_t)(I / 32);
-    int grp[kGuGroups];
-#pragma unroll
-    for (int g = 0; g < kGuGroups; ++g) grp[g] = 16 * b + 4 * wg + g;
+    const int grp[kGuGroups] = {16 * b + 2 * wave, 16 * b + 2 * wave + 1};
 
     for (int c0 = 0; c0 < ne; c0 += kGuChunk) {
         const int nt = min(kGuChunk, ne - c0);
-        int tb, mtw;
-        half_tiles((nt + 15) / 16, hf, &tb, &mtw);
+        const int mt = (nt + 15) / 16;
         const uint16_t *brow = h16 + (size_t)(p0 + c0 + min(16 * wave + (lane >> 2), nt - 1)) * I;
-        f32x4 acc[kGuGroups][4];
+        f32x4 acc[kGuGroups][kGuTiles];
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 0) stage_barrier();
         int bexp[kGuGroups];
-        auto run = [&](auto mtc) {
+        with_tiles(mt, [&](auto mtc) {
             gu_pipeline<true, decltype(mtc)::value>(codes, codes + (size_t)H * I / 2, kt, I / 128,
-                                                    grp, lds, brow, wave, lane, tb, acc, bexp);
-        };
-        switch (mtw) {
-            case 0: run(std::integral_constant<int, 0>{}); break;
-            case 1: run(std::integral_constant<int, 1>{}); break;
-            case 2: run(std::integral_constant<int, 2>{}); break;
-            case 3: run(std::integral_constant<int, 3>{}); break;
-            default: run(std::integral_constant<int, 4>{}); break;
-        }
-        int hs[4];  // row exponents of the lane's tokens, fetched together
+                                                    grp, lds, brow, wave, lane, acc, bexp);
+        });
+        int hs[kGuTiles];  // row exponents of the lane's tokens, fetched together
 #pragma unroll
-        for (int t = 0; t < 4; ++t) hs[t] = hexp[p0 + c0 + min(16 * (tb + t) + n, nt - 1)] - 127;
+        for (int t = 0; t < kGuTiles; ++t) hs[t] = hexp[p0 + c0 + min(16 * t + n, nt - 1)] - 127;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int m = 16 * (tb + t) + n;
-            if (t < mtw && m < nt) {
+        for (int t = 0; t < kGuTiles; ++t) {
+            const int m = 16 * t + n;
+            if (t < mt && m < nt) {
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
                 for (int g = 0; g < kGuGroups; ++g) {
