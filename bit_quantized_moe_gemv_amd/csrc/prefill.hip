@@ -205,13 +205,16 @@ __device__ __forceinline__ uint32_t byte_max(uint32_t w) {
     return max(max(w & 0xFFu, (w >> 8) & 0xFFu), max((w >> 16) & 0xFFu, w >> 24));
 }
 
-template <bool F16, int MT>
+// BCOPY: this wave copies its 16 token rows of the B stage (waves whose rows
+// lie past the pass's last token copy nothing; their count of loads per step
+// is a compile-time constant too).
+template <bool F16, int MT, bool BCOPY>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
                                             int nsuper, const int (&grp)[kGuGroups],
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
                                             f32x4 (&acc)[kGuGroups][kGuTiles],
                                             int (&b)[kGuGroups]) {
-    constexpr int C = 4 + 1 + kGuGroups;  // loads per wave per step
+    constexpr int C = (BCOPY ? 4 : 0) + 1 + kGuGroups;  // loads per wave per step
     uint4 ring[kGuRing][kGuGroups];
     uint32_t goff[kGuGroups];
     const uint32_t soff =
@@ -223,9 +226,11 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
         // B: copy i of this wave moves chunk group i of tokens 16w..16w+15;
         // lane l (token 16w + l/4) fills position l%4
         const int swz = (lane & 3) ^ ((lane >> 4) & 3);  // chunk within the group
+        if constexpr (BCOPY) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            copy_lds16(brow + 128 * J + 8 * (4 * i + swz), lds.b[slot][i][16 * wave]);
+            for (int i = 0; i < 4; ++i)
+                copy_lds16(brow + 128 * J + 8 * (4 * i + swz), lds.b[slot][i][16 * wave]);
+        }
         // scales: lane l copies rows 4(l%4)..+3 of tile 4J + (l/4)%4 of group (l/16)%2
         copy_lds4(scales + soff + (size_t)J * 64, lds.sc[slot][wave]);
 #pragma unroll
@@ -272,18 +277,26 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
     wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
 }
 
-// Runs f(integral_constant<int, mt>) for a tile count mt in 1..kGuTiles.
+// Runs f(integral_constant<int, mt>, integral_constant<bool, copies>) for a
+// tile count mt in 1..kGuTiles; `copies` is whether this wave's token rows
+// (16w..16w+15) hold any of the pass's tokens.
 template <typename F>
-__device__ __forceinline__ void with_tiles(int mt, F &&f) {
+__device__ __forceinline__ void with_tiles(int mt, int wave, F &&f) {
+    auto g = [&](auto mtc) {
+        if (wave < decltype(mtc)::value)
+            f(mtc, std::true_type{});
+        else
+            f(mtc, std::false_type{});
+    };
     switch (mt) {
-        case 1: f(std::integral_constant<int, 1>{}); break;
-        case 2: f(std::integral_constant<int, 2>{}); break;
-        case 3: f(std::integral_constant<int, 3>{}); break;
-        case 4: f(std::integral_constant<int, 4>{}); break;
-        case 5: f(std::integral_constant<int, 5>{}); break;
-        case 6: f(std::integral_constant<int, 6>{}); break;
-        case 7: f(std::integral_constant<int, 7>{}); break;
-        default: f(std::integral_constant<int, 8>{}); break;
+        case 1: g(std::integral_constant<int, 1>{}); break;
+        case 2: g(std::integral_constant<int, 2>{}); break;
+        case 3: g(std::integral_constant<int, 3>{}); break;
+        case 4: g(std::integral_constant<int, 4>{}); break;
+        case 5: g(std::integral_constant<int, 5>{}); break;
+        case 6: g(std::integral_constant<int, 6>{}); break;
+        case 7: g(std::integral_constant<int, 7>{}); break;
+        default: f(std::integral_constant<int, 8>{}, std::true_type{}); break;
     }
 }
 
@@ -319,9 +332,9 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
             for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 0) stage_barrier();  // previous chunk's readers are done with the rings
         int unused[kGuGroups];
-        with_tiles(mt, [&](auto mtc) {
-            gu_pipeline<false, decltype(mtc)::value>(ex, ex + (size_t)I * H, kt, H / 128, grp, lds,
-                                                     brow, wave, lane, acc, unused);
+        with_tiles(mt, wave, [&](auto mtc, auto copies) {
+            gu_pipeline<false, decltype(mtc)::value, decltype(copies)::value>(
+                ex, ex + (size_t)I * H, kt, H / 128, grp, lds, brow, wave, lane, acc, unused);
         });
         // epilogue: lane holds rows 4q..4q+3 of the gate group (acc[0]) and of
         // its up partner (acc[1]) for token 16t + n
@@ -374,9 +387,10 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
             for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (c0 > 0) stage_barrier();
         int bexp[kGuGroups];
-        with_tiles(mt, [&](auto mtc) {
-            gu_pipeline<true, decltype(mtc)::value>(codes, codes + (size_t)H * I / 2, kt, I / 128,
-                                                    grp, lds, brow, wave, lane, acc, bexp);
+        with_tiles(mt, wave, [&](auto mtc, auto copies) {
+            gu_pipeline<true, decltype(mtc)::value, decltype(copies)::value>(
+                codes, codes + (size_t)H * I / 2, kt, I / 128, grp, lds, brow, wave, lane, acc,
+                bexp);
         });
         int hs[kGuTiles];  // row exponents of the lane's tokens, fetched together
 #pragma unroll
