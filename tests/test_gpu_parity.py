@@ -75,12 +75,14 @@ def test_zero_router_sends_all_tokens_to_first_experts(torch_dev, path):
     assert got["counts"][:wl.top_k].tolist() == [wl.tokens] * wl.top_k
 
 
-@pytest.mark.parametrize("t", [64, 65, 80, 97, 128, 129, 241])
+@pytest.mark.parametrize("t", [1, 16, 17, 33, 48, 49, 64, 65, 80, 97, 112, 113, 128, 129, 241])
 def test_prefill_expert_token_counts_around_two_chunks(torch_dev, t):
-    """A zero router gives experts 0..k-1 all t tokens: counts at and around
-    the 64/128-token boundaries where an expert's tokens are split between two
-    blocks (an even split in 16-token tiles for 64 < t <= 128, 64-token chunks
-    alternating between the blocks above)."""
+    """A zero router gives experts 0..k-1 all t tokens: every tile count of a
+    128-token pass (1..8 tiles of 16 tokens), the ragged edges of several, and
+    counts that take a second pass (129, 241).  The tile count is a
+    compile-time parameter of the grouped GEMMs, and the waves whose 16 token
+    rows lie past the pass's last token copy no B rows, so every count here
+    runs a different kernel variant."""
     wl = W.TINY.replace(tokens=t, seed=200 + t)
     wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
     got, _, _ = _full_check(torch_dev, wl, PRE, wr=wr)

@@ -36,12 +36,23 @@ def test_tiny_vq_ragged_token_counts_auto_path(torch_dev, t):
 
 
 def test_tiny_vq_zero_router_multi_chunk(torch_dev):
-    """All tokens on experts 0 and 1: 150 tokens per expert, three 64-token
-    chunks spread over both chunk lanes of each (expert, slice) item."""
+    """All tokens on experts 0 and 1: 150 tokens per expert, a full 128-token
+    pass of each (expert, slice) item and a second one of 22 tokens."""
     wl = W.TINY_VQ.replace(tokens=150, seed=21)
     wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
     got, _, _ = _full_check(torch_dev, wl, PRE, wr=wr)
     assert got["counts"][:2].tolist() == [150, 150]
+
+
+@pytest.mark.parametrize("t", [17, 32, 33, 64, 65, 96, 97, 128, 129])
+def test_tiny_vq_grouped_tile_counts(torch_dev, t):
+    """A zero router gives experts 0 and 1 all t tokens (t > 16: the grouped
+    GEMM): each compiled token-tile count of a pass (2, 4, 6, 8 tiles of 16,
+    the pass's count rounded up to even) at its edges, and a second pass."""
+    wl = W.TINY_VQ.replace(tokens=t, seed=300 + t)
+    wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
+    got, _, _ = _full_check(torch_dev, wl, PRE, wr=wr)
+    assert got["counts"][:2].tolist() == [t, t]
 
 
 def test_tiny_vq_zero_input(torch_dev):
