@@ -9,7 +9,7 @@
 // per pass over the slice, so the slice leaves HBM once.
 //
 // Shape of a kernel: one block of eight waves per CU, at most 256 registers
-// per wave and 102 KiB of LDS.  Each wave owns 2 row groups (16 weight rows
+// per wave and 136 KiB of LDS.  Each wave owns 2 row groups (16 weight rows
 // each; for gate/up a gate group and its up partner) and all of the pass's
 // 16-token tiles, so no two waves load or dequantise the same weights.  Per K
 // step of 128 columns each wave issues, in a fixed order, its copies of the B
@@ -119,13 +119,13 @@ __device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
 // the expert's tokens, 128 per pass; wave w computes gate group 8b+w and its
 // up partner for every 16-token tile of the pass.  Per 128-column step every
 // wave issues its four 1 KiB pieces of the B stage, the scales of its 2
-// groups, then its 2 code loads, kGuRing-1 steps ahead, branch-free so the
-// wait counts stay exact.
+// groups, then its 2 code loads, for the step three ahead, at a barrier in the
+// middle of the current step; branch-free, so the wait counts stay exact.
 // ---------------------------------------------------------------------------
 constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * 64;
 constexpr int kGuGroups = 2;   // row groups per wave
-constexpr int kGuRing = 3;
+constexpr int kGuRing = 4;
 constexpr int kGuChunk = 128;  // tokens per pass over the weight slice
 constexpr int kGuTiles = kGuChunk / 16;
 
@@ -142,79 +142,35 @@ struct GuLds {
     uint8_t sc[kGuRing][kGuWaves][256];     // 2 KiB per slot
 };
 
-// MFMAs of one step for one wave: 4 K steps x 2 groups x MT token tiles.  MT
-// is a template parameter (the chunk's tile count, dispatched once per
-// chunk): with a run-time count every tile's MFMAs sat in a basic block of
-// their own, and the compiler could not interleave them with the next K
-// step's LDS reads and conversions.  The next K step's B operands and
-// dequantised A operands are prepared before the current K step's MFMAs
-// (double buffering).
-// F16: fp16 operands, the weights scaled relative to the group exponents b[g].
-template <bool F16, int MT>
-__device__ __forceinline__ void gu_step(const uint4 (&code)[kGuGroups], const GuLds &lds,
-                                        int slot, int wave, int lane,
-                                        const int (&b)[kGuGroups],
-                                        f32x4 (&acc)[kGuGroups][kGuTiles]) {
-    using V8 = std::conditional_t<F16, f16x8, bf16x8>;
-    const int q = lane >> 4, n = lane & 15;
-    float scale[kGuGroups];
-#pragma unroll
-    for (int g = 0; g < kGuGroups; ++g) {
-        const uint32_t e = lds.sc[slot][wave][64 * g + 16 * q + n];
-        scale[g] = F16 ? e8m0_rel_f32(e, b[g]) : e8m0_to_f32(e);
-    }
-    V8 a[2][kGuGroups];
-    V8 bv[2][MT];
-    auto load_b = [&](int buf, int ks) {  // token 16t + n, chunk 4q + ks
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-            bv[buf][t] = *reinterpret_cast<const V8 *>(
-                &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
-    };
-    auto dequant = [&](int buf, int ks) {
-#pragma unroll
-        for (int g = 0; g < kGuGroups; ++g) {
-            const uint4 c = code[g];
-            const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
-            if constexpr (F16)
-                a[buf][g] = fp4x8_to_f16x8(d, scale[g]);
-            else
-                a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
-        }
-    };
-    load_b(0, 0);
-    dequant(0, 0);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int cur = ks & 1;
-        if (ks < 3) {
-            load_b(cur ^ 1, ks + 1);
-            dequant(cur ^ 1, ks + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int g = 0; g < kGuGroups; ++g)
-                acc[g][t] = mfma_op(a[cur][g], bv[cur][t], acc[g][t]);
-    }
-    __builtin_amdgcn_s_setprio(0);
-}
-
 __device__ __forceinline__ uint32_t byte_max(uint32_t w) {
     return max(max(w & 0xFFu, (w >> 8) & 0xFFu), max((w >> 16) & 0xFFu, w >> 24));
 }
 
+// The pipeline of one pass for one wave.  Per step (128 columns): 4 K steps x
+// 2 groups x MT token tiles of MFMAs.  MT is a template parameter (the pass's
+// tile count): with a run-time count every tile's MFMAs sat in a basic block
+// of their own, and the compiler could not interleave them with the next K
+// step's LDS reads and conversions.  The next K step's B operands and
+// dequantised A operands are prepared before the current K step's MFMAs
+// (double buffering), across step boundaries too: the barrier that publishes
+// step J+1 sits between K steps 1 and 2 of step J, and the first operands of
+// step J+1 are prepared under the MFMAs of step J's last K step, so no step
+// starts with the matrix cores idle.  Four LDS slots: step J being read, J+1
+// published, J+2 landing, J+3 issued at that barrier (two steps ahead).
 // BCOPY: this wave copies its 16 token rows of the B stage (waves whose rows
 // lie past the pass's last token copy nothing; their count of loads per step
 // is a compile-time constant too).
+// F16: fp16 operands, the weights scaled relative to the group exponents b[g].
 template <bool F16, int MT, bool BCOPY>
 __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t *scales, size_t kt,
                                             int nsuper, const int (&grp)[kGuGroups],
                                             GuLds &lds, const uint16_t *brow, int wave, int lane,
                                             f32x4 (&acc)[kGuGroups][kGuTiles],
                                             int (&b)[kGuGroups]) {
+    using V8 = std::conditional_t<F16, f16x8, bf16x8>;
+    static_assert(kGuRing == 4, "slot arithmetic below");
     constexpr int C = (BCOPY ? 4 : 0) + 1 + kGuGroups;  // loads per wave per step
+    const int q = lane >> 4, n = lane & 15;
     uint4 ring[kGuRing][kGuGroups];
     uint32_t goff[kGuGroups];
     const uint32_t soff =
@@ -238,8 +194,9 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
             ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
     };
     const int last = nsuper - 1;
-#pragma unroll
-    for (int j = 0; j < kGuRing - 1; ++j) issue(j, min(j, last));
+    issue(0, 0);
+    issue(1, min(1, last));
+    issue(2, min(2, last));
     if constexpr (F16) {
         // b[g] = the largest E8M0 exponent of row group grp[g] (kt tiles of 16
         // bytes), read while the first steps are in flight (past the last
@@ -264,14 +221,76 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
             b[g] = __builtin_amdgcn_readfirstlane((int)m[g]);
         }
     }
+
+    float scale[kGuGroups];
+    V8 a[2][kGuGroups];
+    V8 bv[2][MT];
+    auto read_scales = [&](int slot) {
+#pragma unroll
+        for (int g = 0; g < kGuGroups; ++g) {
+            const uint32_t e = lds.sc[slot][wave][64 * g + 16 * q + n];
+            scale[g] = F16 ? e8m0_rel_f32(e, b[g]) : e8m0_to_f32(e);
+        }
+    };
+    auto load_b = [&](int buf, int slot, int ks) {  // token 16t + n, chunk 4q + ks
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            bv[buf][t] = *reinterpret_cast<const V8 *>(
+                &lds.b[slot][q][16 * t + n][16 * (ks ^ ((n >> 2) & 3))]);
+    };
+    auto dequant = [&](int buf, const uint4 (&code)[kGuGroups], int ks) {
+#pragma unroll
+        for (int g = 0; g < kGuGroups; ++g) {
+            const uint4 c = code[g];
+            const uint32_t d = ks == 0 ? c.x : ks == 1 ? c.y : ks == 2 ? c.z : c.w;
+            if constexpr (F16)
+                a[buf][g] = fp4x8_to_f16x8(d, scale[g]);
+            else
+                a[buf][g] = fp4x8_to_bf16x8(d, scale[g]);
+        }
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int g = 0; g < kGuGroups; ++g)
+                acc[g][t] = mfma_op(a[buf][g], bv[buf][t], acc[g][t]);
+    };
+
+    wait_vmcnt<2 * C>();  // step 0 has landed
+    stage_barrier();
+    read_scales(0);
+    load_b(0, 0, 0);
+    dequant(0, ring[0], 0);
     for (int J0 = 0; J0 < nsuper; J0 += kGuRing) {
 #pragma unroll
         for (int jj = 0; jj < kGuRing; ++jj) {
             const int J = J0 + jj;
-            wait_vmcnt<(kGuRing - 2) * C>();  // step J has landed
-            stage_barrier();
-            issue((jj + kGuRing - 1) % kGuRing, min(J + kGuRing - 1, last));
-            if (J < nsuper) gu_step<F16, MT>(ring[jj], lds, jj, wave, lane, b, acc);
+            const int nx = (jj + 1) % kGuRing;  // slot of step J+1
+            __builtin_amdgcn_s_setprio(1);
+            if (J < nsuper) {
+                load_b(1, jj, 1);
+                dequant(1, ring[jj], 1);
+                mfmas(0);  // K step 0
+                load_b(0, jj, 2);
+                dequant(0, ring[jj], 2);
+                mfmas(1);  // K step 1
+            }
+            __builtin_amdgcn_s_setprio(0);
+            wait_vmcnt<C>();  // step J+1 has landed (step J+2 may be in flight)
+            stage_barrier();  // publishes step J+1; every wave is done with step J-1
+            issue((jj + 3) % kGuRing, min(J + 3, last));
+            __builtin_amdgcn_s_setprio(1);
+            if (J < nsuper) {
+                load_b(1, jj, 3);
+                dequant(1, ring[jj], 3);
+                mfmas(0);  // K step 2
+                read_scales(nx);
+                load_b(0, nx, 0);
+                dequant(0, ring[nx], 0);
+                mfmas(1);  // K step 3
+            }
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     wait_vmcnt<0>();  // the repeated tail loads land before the rings are reused
