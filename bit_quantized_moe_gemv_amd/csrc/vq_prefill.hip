@@ -430,13 +430,10 @@ struct VgLds {
     uint4 b[kVgRing][4][kVgChunk];         // [slot][q][token]: 8 columns of fp16
 };
 
-// One K step S (0..7 of a 256-column super-step) of a wave: 2 groups x MT
-// token tiles.
-template <int S, int MT, bool RES>
-__device__ __forceinline__ void vg_kstep(const uint32_t (&cr)[kVgGroups][6], const VgLds &lds,
-                                         int slot, int lane, f32x4 (&acc)[kVgGroups][MT]) {
-    const int q = lane >> 4, n = lane & 15;
-    uint4 cbv[kVgGroups], rbv[kVgGroups];
+// Book rows of K step S for the wave's 2 groups (issued, not waited for).
+template <int S, bool RES>
+__device__ __forceinline__ void vg_gather(const uint32_t (&cr)[kVgGroups][6], const VgLds &lds,
+                                          uint4 (&cbv)[kVgGroups], uint4 (&rbv)[kVgGroups]) {
 #pragma unroll
     for (int g = 0; g < kVgGroups; ++g) {
         uint32_t i13, i8;
@@ -444,19 +441,38 @@ __device__ __forceinline__ void vg_kstep(const uint32_t (&cr)[kVgGroups][6], con
         cbv[g] = lds.cb[i13];
         if (RES) rbv[g] = lds.rb[i8];
     }
-    uint4 bv[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) bv[t] = lds.b[slot][q][16 * t + n];
-    f16x8 a[kVgGroups];
+}
+
+template <bool RES>
+__device__ __forceinline__ void vg_form_a(const uint4 (&cbv)[kVgGroups],
+                                          const uint4 (&rbv)[kVgGroups], f16x8 (&a)[kVgGroups]) {
 #pragma unroll
     for (int g = 0; g < kVgGroups; ++g)
         a[g] = RES ? add_f16x8(cbv[g], rbv[g]) : __builtin_bit_cast(f16x8, cbv[g]);
+}
+
+// One K step of a wave: 2 groups x MT token tiles with the A operands a
+// (gathered one K step earlier).  The step's B reads go first, then the book
+// gathers of the next K step SN (codes crn), then the MFMAs, which wait for
+// the B reads only (LDS reads complete in order), so the gathers' latency
+// hides under the MFMAs; a then becomes the next step's A.
+template <int SN, int MT, bool RES>
+__device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[kVgGroups][6], const VgLds &lds,
+                                         int slot, int lane, f16x8 (&a)[kVgGroups],
+                                         f32x4 (&acc)[kVgGroups][MT]) {
+    const int q = lane >> 4, n = lane & 15;
+    uint4 bv[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) bv[t] = lds.b[slot][q][16 * t + n];
+    uint4 cbv[kVgGroups], rbv[kVgGroups];
+    vg_gather<SN, RES>(crn, lds, cbv, rbv);
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int g = 0; g < kVgGroups; ++g)
             acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], __builtin_bit_cast(f16x8, bv[t]),
                                                                acc[g][t], 0, 0, 0);
+    vg_form_a<RES>(cbv, rbv, a);
 }
 
 // One pass (at most 128 tokens from route position pc) over the item's rows.
@@ -513,6 +529,12 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
     vq_wait_vmcnt<0>();
     store_b(0);
     load_b(min(1, lastS));
+    f16x8 a[kVgGroups];  // the A operands of the current K step
+    {
+        uint4 cbv[kVgGroups], rbv[kVgGroups];
+        vg_gather<0, RES>(cr[0], lds, cbv, rbv);
+        vg_form_a<RES>(cbv, rbv, a);
+    }
     // Per K step S = 8J+s: B(S+1) (issued at S-1, followed by the code loads
     // of super-step J when S-1 began one) lands and goes to LDS; the barrier
     // publishes B(S); then B(S+2) and, at s = 0, the codes of super-step J+1
@@ -534,15 +556,18 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
                 load_b(min(S + 2, lastS));
                 if (s == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
                 if (J < NJ) {
+                    // the next K step's codes: this super-step's, or at s = 7
+                    // the next super-step's (issued at s = 0, landed by s = 2;
+                    // past the end they repeat the last super-step's)
                     const int slot = S % kVgRing;
-                    if (s == 0) vg_kstep<0, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 1) vg_kstep<1, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 2) vg_kstep<2, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 3) vg_kstep<3, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 4) vg_kstep<4, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 5) vg_kstep<5, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 6) vg_kstep<6, MT, RES>(cr[jj], lds, slot, lane, acc);
-                    if (s == 7) vg_kstep<7, MT, RES>(cr[jj], lds, slot, lane, acc);
+                    if (s == 0) vg_kstep<1, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 1) vg_kstep<2, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 2) vg_kstep<3, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 3) vg_kstep<4, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 4) vg_kstep<5, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 5) vg_kstep<6, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 6) vg_kstep<7, MT, RES>(cr[jj], lds, slot, lane, a, acc);
+                    if (s == 7) vg_kstep<0, MT, RES>(cr[jj ^ 1], lds, slot, lane, a, acc);
                 }
             }
         }
