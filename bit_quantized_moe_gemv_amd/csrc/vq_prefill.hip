@@ -452,18 +452,19 @@ __device__ __forceinline__ void vg_form_a(const uint4 (&cbv)[kVgGroups],
 }
 
 // One K step of a wave: 2 groups x MT token tiles with the A operands a
-// (gathered one K step earlier).  The step's B reads go first, then the book
+// (gathered one K step earlier) and B from the LDS row bq (the step's piece
+// q = lane/16, indexed by token).  The step's B reads go first, then the book
 // gathers of the next K step SN (codes crn), then the MFMAs, which wait for
 // the B reads only (LDS reads complete in order), so the gathers' latency
 // hides under the MFMAs; a then becomes the next step's A.
 template <int SN, int MT, bool RES>
 __device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[kVgGroups][6], const VgLds &lds,
-                                         int slot, int lane, f16x8 (&a)[kVgGroups],
+                                         const uint4 *bq, int lane, f16x8 (&a)[kVgGroups],
                                          f32x4 (&acc)[kVgGroups][MT]) {
-    const int q = lane >> 4, n = lane & 15;
+    const int n = lane & 15;
     uint4 bv[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) bv[t] = lds.b[slot][q][16 * t + n];
+    for (int t = 0; t < MT; ++t) bv[t] = bq[16 * t + n];  // token 16t + n of the lane's piece
     uint4 cbv[kVgGroups], rbv[kVgGroups];
     vg_gather<SN, RES>(crn, lds, cbv, rbv);
 #pragma unroll
@@ -486,10 +487,17 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
                                         const int32_t *__restrict__ bexp,
                                         float *__restrict__ out) {
     const int q = lane >> 4, n = lane & 15;
-    // B staging: wave w moves piece q = w%4 (columns 64q + 8s..+7 of K step
-    // s) of tokens 64(w/4) + lane, one 16-byte register load per K step
+    // An LDS slot holds one K step of 128 tokens ([piece q][token]) or, for
+    // passes of at most 64 tokens, two K steps ([K step][piece q][token]):
+    // then barriers come every two K steps.
+    constexpr int KPS = MT <= 4 ? 2 : 1;  // K steps per slot
+    constexpr int SPS = 8 / KPS;          // slot steps per super-step
+    // B staging: wave w moves piece w%4 (columns 64q + 8s..+7 of K step s) of
+    // tokens 64(w/4) + lane (one K step per slot) or of tokens lane, K step
+    // w/4 of the slot (two), one 16-byte register load per slot step
     const int sq = wave & 3;
-    const int tok = min(64 * (wave >> 2) + lane, nt - 1);
+    const int kw = KPS == 2 ? wave >> 2 : 0;
+    const int tok = min((KPS == 2 ? 0 : 64 * (wave >> 2)) + lane, nt - 1);
     const uint16_t *brow = MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H
                                      : bsrc + (size_t)(pc + tok) * I;
     f32x4 acc[kVgGroups][MT];
@@ -515,59 +523,71 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
             cr[slot][g][5] = p;
         }
     };
+    auto slot_base = [&](int P) { return &lds.b[P % kVgRing][0][0]; };
     uint4 bstage;
-    auto load_b = [&](int S) {  // K step S = 8J + s
+    auto load_b = [&](int P) {  // slot step P; this wave's K step S = KPS*P + kw
+        const int S = KPS * P + kw;
         bstage = *reinterpret_cast<const uint4 *>(brow + 256 * (S >> 3) + 64 * sq + 8 * (S & 7));
     };
-    auto store_b = [&](int S) { lds.b[S % kVgRing][sq][64 * (wave >> 2) + lane] = bstage; };
+    auto store_b = [&](int P) {
+        slot_base(P)[KPS == 2 ? (kw * 4 + sq) * 64 + lane : sq * kVgChunk + 64 * (wave >> 2) + lane] =
+            bstage;
+    };
+    auto b_row = [&](int P, int kk) -> const uint4 * {  // K step kk of slot step P, piece q
+        return slot_base(P) + (KPS == 2 ? (kk * 4 + q) * 64 : q * kVgChunk);
+    };
     constexpr int kCodeLoads = (RES ? 3 : 2) * kVgGroups;
 
     vq_stage_barrier();  // the previous pass's readers are done with the ring
-    const int NS = 8 * NJ, lastS = NS - 1, lastJ = NJ - 1;
+    const int NP = SPS * NJ, lastP = NP - 1, lastJ = NJ - 1;
     issue_codes(0, 0);
     load_b(0);
     vq_wait_vmcnt<0>();
     store_b(0);
-    load_b(min(1, lastS));
+    load_b(min(1, lastP));
     f16x8 a[kVgGroups];  // the A operands of the current K step
     {
         uint4 cbv[kVgGroups], rbv[kVgGroups];
         vg_gather<0, RES>(cr[0], lds, cbv, rbv);
         vg_form_a<RES>(cbv, rbv, a);
     }
-    // Per K step S = 8J+s: B(S+1) (issued at S-1, followed by the code loads
-    // of super-step J when S-1 began one) lands and goes to LDS; the barrier
-    // publishes B(S); then B(S+2) and, at s = 0, the codes of super-step J+1
-    // are issued.  Loads are issued every step (indices clamped past the
-    // end), so the wait counts are exact.
+    // Per slot step P = SPS*J + p: B(P+1) (issued at P-1, followed by the code
+    // loads of super-step J+1 when P-1 began super-step J) lands and goes to
+    // LDS; the barrier publishes B(P); then B(P+2) and, at p = 0, the codes of
+    // super-step J+1 are issued.  Loads are issued every step (indices clamped
+    // past the end), so the wait counts are exact.
     for (int J0 = 0; J0 < NJ; J0 += 2) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int J = J0 + jj;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int S = 8 * J + s;
-                if (s == 1)
+            for (int p = 0; p < SPS; ++p) {
+                const int P = SPS * J + p;
+                if (p == 1)
                     vq_wait_vmcnt<kCodeLoads>();
                 else
                     vq_wait_vmcnt<0>();
-                store_b(min(S + 1, lastS));
+                store_b(min(P + 1, lastP));
                 vq_stage_barrier();
-                load_b(min(S + 2, lastS));
-                if (s == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
+                load_b(min(P + 2, lastP));
+                if (p == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
                 if (J < NJ) {
-                    // the next K step's codes: this super-step's, or at s = 7
-                    // the next super-step's (issued at s = 0, landed by s = 2;
-                    // past the end they repeat the last super-step's)
-                    const int slot = S % kVgRing;
-                    if (s == 0) vg_kstep<1, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 1) vg_kstep<2, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 2) vg_kstep<3, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 3) vg_kstep<4, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 4) vg_kstep<5, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 5) vg_kstep<6, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 6) vg_kstep<7, MT, RES>(cr[jj], lds, slot, lane, a, acc);
-                    if (s == 7) vg_kstep<0, MT, RES>(cr[jj ^ 1], lds, slot, lane, a, acc);
+#pragma unroll
+                    for (int kk = 0; kk < KPS; ++kk) {
+                        // K step s; the next one's codes: this super-step's,
+                        // or at s = 7 the next super-step's (issued at p = 0,
+                        // landed by p = 2; past the end they repeat the last)
+                        const int s = KPS * p + kk;
+                        const uint4 *bq = b_row(P, kk);
+                        if (s == 0) vg_kstep<1, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 1) vg_kstep<2, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 2) vg_kstep<3, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 3) vg_kstep<4, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 4) vg_kstep<5, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 5) vg_kstep<6, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 6) vg_kstep<7, MT, RES>(cr[jj], lds, bq, lane, a, acc);
+                        if (s == 7) vg_kstep<0, MT, RES>(cr[jj ^ 1], lds, bq, lane, a, acc);
+                    }
                 }
             }
         }
