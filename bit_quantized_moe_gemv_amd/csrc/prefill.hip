@@ -13,12 +13,13 @@
 // each; for gate/up a gate group and its up partner) and all of the pass's
 // 16-token tiles, so no two waves load or dequantise the same weights.  Per K
 // step of 128 columns each wave issues, in a fixed order, its copies of the B
-// stage and of its groups' scales (global_load_lds into an LDS ring) and its 2
-// code loads (1 KiB wave loads into a register ring), a fixed number of steps
-// ahead.  Loads are issued unconditionally (past the end they repeat the last
-// step's addresses) so the wait counts are compile-time constants that the
-// compiler tracks exactly; a conditional issue makes it wait for every load in
-// flight.
+// stage (only waves whose token rows hold tokens of the pass) and of its
+// groups' scales (global_load_lds into a 4-slot LDS ring) and its 2 code loads
+// (1 KiB wave loads into a register ring), three steps ahead, at a barrier in
+// the middle of each step.  Loads are issued unconditionally (past the end
+// they repeat the last step's addresses) so the wait counts are compile-time
+// constants that the compiler tracks exactly; a conditional issue makes it
+// wait for every load in flight.
 //
 // Weights are dequantised to bf16 in registers: every E2M1 value times an
 // in-range E8M0 scale is a bf16 value, so the A operand and the products are
