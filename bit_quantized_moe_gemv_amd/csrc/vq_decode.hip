@@ -95,9 +95,16 @@ __device__ __forceinline__ void store_books(VdBooks &bk, int t, const uint4 (&bv
 
 // One K step (vector S of the lane's runs) for G groups against the
 // activation piece b: two fp32 dot products per group, Cb[i13] . b and
-// Rb[i8] . b, each over the eight fp16 pairs with exact products.
+// Rb[i8] . b, each over the eight fp16 pairs with exact products.  Random
+// 16-byte reads are what bound these kernels: from LDS they cost about 5 ns
+// per wave instruction on a CU (bank conflicts), and from the 4 KiB residual
+// book in global memory, which stays in the L1 cache, about 14 ns, but on the
+// vector-memory path, in parallel with LDS.  So odd K steps read Rb from
+// global memory (rbg) and even ones from LDS: about 8 ns per vector pair
+// against 10.5 with both from LDS (measured on a random-gather probe).
 template <int S, int G, bool RES>
-__device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBooks &bk, uint4 b,
+__device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBooks &bk,
+                                         const uint4 *__restrict__ rbg, uint4 b,
                                          float (&acc)[G][2]) {
     uint4 cbv[G], rbv[G];
 #pragma unroll
@@ -105,7 +112,7 @@ __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBoo
         uint32_t i13, i8;
         vq_indices<S>(cr[g], i13, i8);
         cbv[g] = bk.cb[i13];
-        if (RES) rbv[g] = bk.rb[i8];
+        if (RES) rbv[g] = (S & 1) ? rbg[i8] : bk.rb[i8];
     }
     const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -132,15 +139,16 @@ __device__ __forceinline__ void vd_kstep(const uint32_t (&cr)[G][6], const VdBoo
 
 template <int G, bool RES>
 __device__ __forceinline__ void vd_tile(const uint32_t (&cr)[G][6], const VdBooks &bk,
+                                        const uint4 *__restrict__ rbg,
                                         const uint4 *bpieces, int q, float (&acc)[G][2]) {
-    vd_kstep<0, G, RES>(cr, bk, bpieces[0 * 4 + q], acc);
-    vd_kstep<1, G, RES>(cr, bk, bpieces[1 * 4 + q], acc);
-    vd_kstep<2, G, RES>(cr, bk, bpieces[2 * 4 + q], acc);
-    vd_kstep<3, G, RES>(cr, bk, bpieces[3 * 4 + q], acc);
-    vd_kstep<4, G, RES>(cr, bk, bpieces[4 * 4 + q], acc);
-    vd_kstep<5, G, RES>(cr, bk, bpieces[5 * 4 + q], acc);
-    vd_kstep<6, G, RES>(cr, bk, bpieces[6 * 4 + q], acc);
-    vd_kstep<7, G, RES>(cr, bk, bpieces[7 * 4 + q], acc);
+    vd_kstep<0, G, RES>(cr, bk, rbg, bpieces[0 * 4 + q], acc);
+    vd_kstep<1, G, RES>(cr, bk, rbg, bpieces[1 * 4 + q], acc);
+    vd_kstep<2, G, RES>(cr, bk, rbg, bpieces[2 * 4 + q], acc);
+    vd_kstep<3, G, RES>(cr, bk, rbg, bpieces[3 * 4 + q], acc);
+    vd_kstep<4, G, RES>(cr, bk, rbg, bpieces[4 * 4 + q], acc);
+    vd_kstep<5, G, RES>(cr, bk, rbg, bpieces[5 * 4 + q], acc);
+    vd_kstep<6, G, RES>(cr, bk, rbg, bpieces[6 * 4 + q], acc);
+    vd_kstep<7, G, RES>(cr, bk, rbg, bpieces[7 * 4 + q], acc);
 }
 
 // A row's dot product from its four lanes (n, q = 0..3): every lane of row n
@@ -178,6 +186,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, n = lane & 15;
+    const uint4 *rbg = reinterpret_cast<const uint4 *>(packed) + kVqEntries;  // Rb in memory
     const int wa = min(wave, NWA - 1);
     const int gset = wa / NSL, js = wa % NSL;  // groups [gset*GW, +GW), tiles [js*TJ, +TJ)
 
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     for (int g = 0; g < GW; ++g) acc[g][0] = acc[g][1] = 0.f;
 #pragma unroll
     for (int u = 0; u < TJ; ++u)
-        vd_tile<GW, RES>(cr[u], lds.bk, &lds.x16[32 * (js * TJ + u)], q, acc);
+        vd_tile<GW, RES>(cr[u], lds.bk, rbg, &lds.x16[32 * (js * TJ + u)], q, acc);
 
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
@@ -305,6 +314,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, n = lane & 15;
+    const uint4 *rbg = reinterpret_cast<const uint4 *>(packed) + kVqEntries;  // Rb in memory
     const int rg = blockIdx.x;
     const int NJD = I / 256;
     const int r4 = wave & 3, jq = wave >> 2;
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
         float a1[1][2] = {{0.f, 0.f}};
 #pragma unroll
         for (int u = 0; u < TJ; ++u)
-            vd_tile<1, RES>(cr[f][u], lds.bk, &lds.h16[r4][32 * (j0 + u)], q, a1);
+            vd_tile<1, RES>(cr[f][u], lds.bk, rbg, &lds.h16[r4][32 * (j0 + u)], q, a1);
         acc[f] = row_sum(a1[0]);
     }
 
