@@ -152,23 +152,25 @@ class Bench:
         return big, int(big.data_ptr()), stride, n
 
     def vq_layers(self):
-        """One device copy of the VQ13R8 layer (2.1 GB: larger than every cache)."""
+        """--layers device copies of the VQ13R8 layer (2.1 GB each), cycled like the
+        MXFP4 copies so that replayed stages do not find the last launch's
+        experts in the last-level cache."""
         if not hasattr(self, "_vq"):
             W, torch = self.W, self.torch
             log(f"generating the MiMo-shaped VQ13R8 layer ({W.VQ_PREFILL.packed_bytes} B)")
             host = W.make_experts(W.VQ_PREFILL)
-            self._vq = self._copies(host, 1)
+            self._vq = self._copies(host, self.args.layers)
             del host
             torch.cuda.synchronize()
         return self._vq
 
     def vq13_layers(self):
-        """One device copy of the VQ13 layer (1.3 GB: larger than every cache)."""
+        """--layers device copies of the VQ13 layer (1.3 GB each), cycled."""
         if not hasattr(self, "_vq13"):
             W, torch = self.W, self.torch
             log(f"generating the MiMo-shaped VQ13 layer ({W.VQ13_DECODE.packed_bytes} B)")
             host = W.make_experts(W.VQ13_DECODE)
-            self._vq13 = self._copies(host, 1)
+            self._vq13 = self._copies(host, self.args.layers)
             del host
             torch.cuda.synchronize()
         return self._vq13
@@ -218,7 +220,7 @@ class Bench:
         return round(us, 3)
 
     def run(self, wl, steps, warmup, tokens_per_step, profile=True, layers=None, replay=0,
-            path=0):
+            path=0, clock_warmup_s=0.0):
         torch, bq, W = self.torch, self.bq, self.W
         T = tokens_per_step
         n_batches = steps + warmup
@@ -249,6 +251,18 @@ class Bench:
                 if rc != 0:
                     raise bq.MoeError(rc, "moe_layer_forward")
 
+        if clock_warmup_s > 0:
+            # untimed forwards over the warm-up tokens (cycling the layer
+            # copies) until the GPU has run for clock_warmup_s, so that the
+            # timed steps do not start at an idle clock
+            t_end, i = time.perf_counter() + clock_warmup_s, 0
+            while time.perf_counter() < t_end:
+                for _ in range(64):
+                    rc = layer.forward_raw(xp[i % max(1, warmup)], T, wp, lp[i % L], op, st)
+                    if rc != 0:
+                        raise bq.MoeError(rc, "moe_layer_forward")
+                    i += 1
+                torch.cuda.synchronize()
         loop(0, warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -411,6 +425,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--layers", type=int, default=8, help="device copies of the layer cycled")
+    ap.add_argument("--clock-warmup", type=float, default=0.3,
+                    help="seconds of untimed decode steps before the warm-up steps of the "
+                         "headline workload (the GPU clock ramps up under load)")
     ap.add_argument("--cpu-tokens", type=int, default=12, help="oracle tokens per run")
     ap.add_argument("--cpu-runs", type=int, default=5, help="oracle runs (median)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -466,7 +483,8 @@ def main():
         return
 
     log("decode T=1")
-    dec = b.run(W.DECODE, args.steps, args.warmup, 1, replay=args.steps)
+    dec = b.run(W.DECODE, args.steps, args.warmup, 1, replay=args.steps,
+                clock_warmup_s=args.clock_warmup)
     wl = W.DECODE
     alg = algorithmic(wl, dec["distinct_experts_last_step"], 1)
     gu_us = dec["replay_us"]["gateup"]
@@ -493,8 +511,8 @@ def main():
         pre = b.run(W.PREFILL, 30, 5, 2048, replay=10)
         extra["prefill_t2048"] = prefill_report(pre, algorithmic(W.PREFILL, W.PREFILL.experts, 2048))
         log("VQ13R8 decode T=1")
-        vqd = b.run(W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1"), 200, 20, 1,
-                    layers=b.vq_layers(), replay=100)
+        vqd = b.run(W.VQ_PREFILL.replace(tokens=1, name="mimo_vq_decode_t1"), 1000, 200, 1,
+                    layers=b.vq_layers(), replay=500)
         extra["vq_decode_t1"] = vqd
         log("VQ13R8 verify T=16 (skewed routing)")
         vqv = b.run(W.VERIFY.replace(fmt=W.FMT_VQ13R8, name="mimo_vq_verify_t16_skewed"), 100, 10,
@@ -515,8 +533,8 @@ def main():
             sweep[f"t{t}"] = row
         extra["verify_width_sweep"] = sweep
         log("VQ13 decode T=1")
-        extra["vq13_decode_t1"] = b.run(W.VQ13_DECODE, 200, 20, 1, layers=b.vq13_layers(),
-                                        replay=100)
+        extra["vq13_decode_t1"] = b.run(W.VQ13_DECODE, 1000, 200, 1, layers=b.vq13_layers(),
+                                        replay=500)
         log("VQ13R8 prefill T=2048")
         vq = b.run(W.VQ_PREFILL, 30, 5, 2048, layers=b.vq_layers(), replay=10)
         extra["vq_prefill_t2048"] = prefill_report(
