@@ -67,6 +67,7 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     if (is_vq_format(s.fmt)) {
         b += align256((size_t)tmax * s.H * 2);  // x16
         b += align256((size_t)tmax * 4);        // xexp
+        b += align256(R * (s.I / 64) * 4);      // hpmax
     }
     return b;
 }
@@ -93,9 +94,11 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));
     ws->x16 = nullptr;
     ws->xexp = nullptr;
+    ws->hpmax = nullptr;
     if (is_vq_format(s.fmt)) {
         ws->x16 = reinterpret_cast<uint16_t *>(take((size_t)tmax * s.H * 2));
         ws->xexp = reinterpret_cast<int32_t *>(take((size_t)tmax * 4));
+        ws->hpmax = reinterpret_cast<float *>(take(R * (s.I / 64) * 4));
     }
 }
 

@@ -56,6 +56,9 @@ struct Workspace {
     int32_t *xexp;     // [Tmax]
     uint16_t *h16;     // [Rmax][I]
     int32_t *hexp;     // [Rmax]
+    // VQ only (null otherwise): the largest |h| of each 64-column piece of a
+    // route's h row, written by the batch-1 VQ gate/up blocks for the down kernel
+    float *hpmax;      // [Rmax][I/64]
 };
 
 size_t workspace_bytes(const Shape &s, int tmax);

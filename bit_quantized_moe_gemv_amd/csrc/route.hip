@@ -10,6 +10,7 @@
 // multiply-adds in ascending column order; the wave then adds partials with an
 // xor butterfly, which forms exactly the pairwise tree of adjacent blocks.
 #include "moe_internal.h"
+#include "vq_common.h"
 
 namespace bqmoe {
 
@@ -184,7 +185,10 @@ __device__ int block_exclusive_scan(int v, int *total, int *lds /* >= 16 ints */
 //
 // router_small_kernel: each wave computes one expert's logits for up to TT
 // tokens, with every load (MAXG 256-column groups of W and x) issued before the
-// first FMA, in the same summation order as router_kernel.
+// first FMA, in the same summation order as router_kernel.  With xexp (VQ
+// layers) the wave of expert 0 also writes each token's fp16 row exponent
+// (its largest |x| scaled into [2^14, 2^15)), which the batch-1 VQ gate/up
+// kernel needs before its first barrier.
 //
 // route_small_kernel (one block of 16 waves): top-k and weights, one wave per
 // token; a 16-bit mask per expert of the tokens routed to it (LDS atomic or);
@@ -262,7 +266,8 @@ template <int TT, int MAXG>
 __global__ __launch_bounds__(64 * kRsWaves) void router_small_kernel(const uint16_t *__restrict__ x,
                                                            const float *__restrict__ wr, int T,
                                                            int H, int E,
-                                                           float *__restrict__ logits) {
+                                                           float *__restrict__ logits,
+                                                           int32_t *__restrict__ xexp) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.y * kRsWaves + (threadIdx.x >> 6);
     const int t0 = blockIdx.x * TT;
@@ -280,6 +285,24 @@ __global__ __launch_bounds__(64 * kRsWaves) void router_small_kernel(const uint1
         for (int j = 0; j < MAXG; ++j)
             if (j < groups && t0 + t < T)
                 xb[t][j] = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + t) * H + (j << 8) + (lane << 2));
+    if (xexp != nullptr && e == 0) {  // wave-uniform; x arrives before the W row
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if (t0 + t >= T) break;
+            uint32_t mb = 0;  // largest |x| as fp32 bits (bf16 bits shifted up)
+#pragma unroll
+            for (int j = 0; j < MAXG; ++j) {
+                if (j < groups) {
+                    mb = max(mb, (xb[t][j].x & 0x7FFFu) << 16);
+                    mb = max(mb, xb[t][j].x & 0x7FFF0000u);
+                    mb = max(mb, (xb[t][j].y & 0x7FFFu) << 16);
+                    mb = max(mb, xb[t][j].y & 0x7FFF0000u);
+                }
+            }
+            const float xm = wave_max_f32(__uint_as_float(mb));
+            if (lane == 0) xexp[t0 + t] = fp16_row_exponent(__float_as_uint(xm));
+        }
+    }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         if (t0 + t >= T) break;
@@ -300,23 +323,26 @@ __global__ __launch_bounds__(64 * kRsWaves) void router_small_kernel(const uint1
 
 template <int TT>
 static void router_small_launch(const Shape &s, dim3 grid, hipStream_t st, const uint16_t *x,
-                                const float *wr, int T, float *logits) {
+                                const float *wr, int T, float *logits, int32_t *xexp) {
     const int g = s.H / 256;
     constexpr int nt = 64 * kRsWaves;
-    if (g <= 1) router_small_kernel<TT, 1><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else if (g <= 4) router_small_kernel<TT, 4><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else if (g <= 16) router_small_kernel<TT, 16><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
-    else router_small_kernel<TT, 32><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits);
+    if (g <= 1) router_small_kernel<TT, 1><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits, xexp);
+    else if (g <= 4) router_small_kernel<TT, 4><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits, xexp);
+    else if (g <= 16) router_small_kernel<TT, 16><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits, xexp);
+    else router_small_kernel<TT, 32><<<grid, nt, 0, st>>>(x, wr, T, s.H, s.E, logits, xexp);
 }
 
 hipError_t launch_router_route_small(const Shape &s, const uint16_t *x, const float *wr, int T,
                                      const Workspace &ws, hipStream_t st, bool route_single) {
     if (T < 1 || T > kDecodeMaxTokens || s.H / 256 > 32) return hipErrorInvalidValue;
     const int ey = (s.E + kRsWaves - 1) / kRsWaves;
+    // the fp16 row exponents of x feed the batch-1 VQ kernels (a VQ workspace
+    // has xexp; for larger VQ batches the x packing kernel rewrites them)
+    int32_t *xexp = is_vq_format(s.fmt) ? ws.xexp : nullptr;
     if (T == 1)
-        router_small_launch<1>(s, dim3(1, ey), st, x, wr, T, ws.logits);
+        router_small_launch<1>(s, dim3(1, ey), st, x, wr, T, ws.logits, xexp);
     else
-        router_small_launch<4>(s, dim3((T + 3) / 4, ey), st, x, wr, T, ws.logits);
+        router_small_launch<4>(s, dim3((T + 3) / 4, ey), st, x, wr, T, ws.logits, xexp);
     hipError_t e = hipGetLastError();
     // a single token is routed by the batch-1 gate/up kernel unless route_single
     if (e != hipSuccess || (T == 1 && !route_single)) return e;

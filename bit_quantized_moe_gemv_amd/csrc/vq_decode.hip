@@ -19,7 +19,11 @@
 //
 // Every barrier in these kernels orders LDS only (lds_barrier): a full
 // __syncthreads() would also wait for every global load in flight, i.e. the
-// block's whole index stream, before the first gather.
+// block's whole index stream, before the first gather.  Index loads are
+// issued after the last barrier that precedes the gathers: issuing them
+// stalls while the HBM stream is saturated, so a barrier behind them would
+// hold every wave's gathers until the slowest wave had issued all of its
+// loads.
 //
 // Kernels (one token, k routes):
 //  * vq_dec_gateup: block = 4 (gate, up) row-group pairs of one route (8
@@ -28,12 +32,15 @@
 //    2^s_x and SwiGLU, writing h (fp32, route-position order).  Every block
 //    finds its expert from the router logits itself (one wave, the selected
 //    set only); block 0 runs the ordered top-k with its weights and publishes
-//    the routing.
+//    the routing.  The activation's fp16 exponent s_x comes from the router
+//    kernel, so x16 is staged in LDS before the block's first barrier.
 //  * vq_dec_down: block = one output row group (16 rows) for all k routes.
 //    Each wave streams one route's tiles over a quarter of K; the routes go
 //    through in two phases of four, h of the phase's routes staged in LDS as
-//    fp16 with a per-route exponent (the books leave room for four).  The
-//    block sums the weighted contributions in a fixed order and stores out.
+//    fp16 with a per-route exponent (the books leave room for four), taken
+//    from the largest |h| of each 64-column piece that the gate/up blocks
+//    leave beside h.  The block sums the weighted contributions in a fixed
+//    order and stores out.
 #include "vq_common.h"
 
 namespace bqmoe {
@@ -54,7 +61,6 @@ struct VdGuLds {
     VdBooks bk;
     uint4 x16[kVdMaxH / 8];   // fp16 x * 2^-s, piece (J, s, q) at (8J + s)*4 + q
     float red[kVdWaves][kVdGroups][16];  // [K slice][group][row]
-    float wmax[kVdWaves];
     int expert;
 };
 
@@ -62,7 +68,6 @@ struct VdDnLds {
     VdBooks bk;
     uint4 h16[4][kVdMaxI / 8];  // one phase's 4 routes, fp16 h * 2^-s, same piece order
     float red[kVdWaves][16];    // [wave][row]
-    uint32_t rmax[8];           // per route: largest |h| (fp32 bits)
 };
 
 // The books reach LDS through registers: each of NT threads loads kBookLoads
@@ -174,11 +179,12 @@ __device__ __forceinline__ int piece_elem(int c) {
 // ---------------------------------------------------------------------------
 template <int GW, int TJ, int NSL, bool RES>
 __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed, size_t expert_bytes, int H,
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ xexp,
+    const uint8_t *__restrict__ packed, size_t expert_bytes, int H,
     int I, int E, int K, const float *__restrict__ logits, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ active, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-    float *__restrict__ h, bool sigmoid) {
+    float *__restrict__ h, float *__restrict__ hpmax, bool sigmoid) {
     constexpr int NJ = NSL * TJ;
     constexpr int NWA = NSL * (kVdGroups / GW);  // waves with work
     static_assert(kVdGroups % GW == 0 && NWA <= kVdWaves, "wave split");
@@ -197,6 +203,10 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     const int i0 = (kVdPairs * blockIdx.x) % ipg;
     const int nx = H / 8;
     const uint4 xv = reinterpret_cast<const uint4 *>(x)[min(tid, nx - 1)];
+    // x's fp16 row exponent s_x (largest |x| scaled into [2^14, 2^15)), written
+    // by the router kernel: x16 is staged before the first barrier, so no
+    // barrier separates the index loads from the gathers
+    const int xs = __builtin_amdgcn_readfirstlane(xexp[0]);
     if (wave == 0) {
         float lv[4];
         topk_load(logits, E, lv);
@@ -222,17 +232,20 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         load_books<kVdThreads - 64, RES>(packed, tid - 64, bv);
         store_books<kVdThreads - 64, RES>(lds.bk, tid - 64, bv);
     }
-    uint32_t mb = 0;  // largest |x| bits of the thread's 8 values
-    {
+    // x -> fp16 * 2^-s_x
+    if (tid < nx) {
         const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            mb = max(mb, (w4[k] & 0x7FFFu) << 16);
-            mb = max(mb, w4[k] & 0x7FFF0000u);
+            const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(w4[k] & 0xFFFFu), -xs);
+            const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(w4[k] >> 16), -xs);
+            o[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
+        reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(lds.x16) + piece_elem(8 * tid))[0] =
+            make_uint4(o[0], o[1], o[2], o[3]);
     }
-    const float wm = wave_max_f32(__uint_as_float(mb));
-    if (lane == 0) lds.wmax[wave] = wm;
     lds_barrier();
     const int e = __builtin_amdgcn_readfirstlane(lds.expert);
 
@@ -250,26 +263,6 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
     // the row gains of the epilogue (thread t < 64: pair t/16, row t%16)
     const int grow = 16 * (i0 + ((tid >> 4) & (kVdPairs - 1))) + (tid & 15);
     const uint32_t gg = m.gain[grow], gu = m.gain[I + grow];
-
-    // x -> fp16 * 2^-s_x, s_x from the row's largest magnitude
-    float xm = lds.wmax[0];
-#pragma unroll
-    for (int w2 = 1; w2 < kVdWaves; ++w2) xm = fmaxf(xm, lds.wmax[w2]);
-    const int xs = fp16_row_exponent(__float_as_uint(xm));
-    if (tid < nx) {
-        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(w4[k] & 0xFFFFu), -xs);
-            const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(w4[k] >> 16), -xs);
-            o[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(lds.x16) + piece_elem(8 * tid))[0] =
-            make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    lds_barrier();
 
     float acc[GW][2];
 #pragma unroll
@@ -294,7 +287,13 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_gateup(
         }
         const float gv = ldexpf(gs * f16_bits_to_f32(gg), xs);
         const float uv = ldexpf(us * f16_bits_to_f32(gu), xs);
-        h[(size_t)p * I + grow] = silu_f32(gv) * uv;
+        const float hv = silu_f32(gv) * uv;
+        h[(size_t)p * I + grow] = hv;
+        // the block's 64 h values are one 64-column piece of the route's row:
+        // its largest |h| lets the down kernel pick the row's fp16 exponent
+        // without a block-wide reduction (threads 0..63 are wave 0)
+        const float hm = wave_max_f32(fabsf(hv));
+        if (tid == 0) hpmax[(size_t)p * (I / 64) + i0 / 4] = hm;
     }
 }
 
@@ -309,7 +308,8 @@ template <int TJ, bool RES>
 __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K,
     const int32_t *__restrict__ active, const int32_t *__restrict__ perm,
-    const float *__restrict__ wts, const float *__restrict__ h, float *__restrict__ out) {
+    const float *__restrict__ wts, const float *__restrict__ h, const float *__restrict__ hpmax,
+    float *__restrict__ out) {
     __shared__ __align__(16) VdDnLds lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -321,7 +321,6 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
     const bool jlive = jq * TJ < NJD;
     const int j0 = min(jq * TJ, NJD - TJ);  // clamped for loads
 
-    if (tid < 8) lds.rmax[tid] = 0;
     uint4 bv[kBookLoads];
     load_books<kVdThreads, RES>(packed, tid, bv);
     int ex[2];
@@ -340,39 +339,31 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         hv[k] = reinterpret_cast<const float4 *>(h + (size_t)min(4 * hh + k, K - 1) * I)[cg];
-
-    const size_t dn_off = vq_down_offset((size_t)H, (size_t)I, RES);
-    uint32_t cr[2][TJ][1][6];
+    // per-route exponents from the largest |h|: the gate/up blocks left the
+    // maxima of the NP = I/64 pieces of each route's row, [route][piece]; lane
+    // l takes pieces 4l..4l+3 of the flattened array (one route: NP is a
+    // multiple of 4), the lanes of a route combine by xor steps, and lane
+    // r*NP/4 ends with route r's maximum (max is exact in any order)
+    const int NP = I / 64, LPR = NP / 4;  // lanes per route
+    const int pl = min(4 * lane, K * NP - 4);
+    const float4 pm = *reinterpret_cast<const float4 *>(hpmax + pl);
+    float rm = fmaxf(fmaxf(pm.x, pm.y), fmaxf(pm.z, pm.w));
+    for (int o = 1; o < LPR; o <<= 1) rm = fmaxf(rm, __shfl_xor(rm, o, kWave));
+    int hs[2][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        hs[r >> 2][r & 3] = fp16_row_exponent(
+            __float_as_uint(__shfl(rm, min(r, K - 1) * LPR, kWave)));
     uint32_t gn[2];  // gain of row 16rg + n
+    const size_t dn_off = vq_down_offset((size_t)H, (size_t)I, RES);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const VqMatrix<RES> m(packed + vq_books_bytes<RES>() + (size_t)ex[f] * expert_bytes + dn_off,
                               (size_t)H, (size_t)I);
-#pragma unroll
-        for (int u = 0; u < TJ; ++u) m.load((size_t)rg * NJD + j0 + u, lane, cr[f][u][0]);
         gn[f] = m.gain[16 * rg + n];
     }
 
-    store_books<kVdThreads, RES>(lds.bk, tid, bv);
-    lds_barrier();
-    // per-route exponents from the largest |h| (non-negative floats order as
-    // their bit patterns)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float a = fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)),
-                              fmaxf(fabsf(hv[k].z), fabsf(hv[k].w)));
-        const float mx = wave_max_f32(a);
-        if (lane == 0) atomicMax(&lds.rmax[4 * hh + k], __float_as_uint(mx));
-    }
-    lds_barrier();
-    int hs[2][4];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) hs[r >> 2][r & 3] = fp16_row_exponent(lds.rmax[r]);
-
-    float acc[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        if (f > 0) lds_barrier();  // phase 0's readers are done with h16
+    auto stage_h16 = [&](int f) {  // the phase's 4 routes of h as fp16 * 2^-s
         if (hh == f) {
             const int pe = piece_elem(4 * cg);
 #pragma unroll
@@ -387,7 +378,29 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
                                    ((uint32_t)__builtin_bit_cast(uint16_t, d) << 16));
             }
         }
-        lds_barrier();
+    };
+    store_books<kVdThreads, RES>(lds.bk, tid, bv);
+    stage_h16(0);
+    lds_barrier();  // books and phase 0's h16
+
+    // the index streams of both phases, issued after the barrier (see above)
+    uint32_t cr[2][TJ][1][6];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const VqMatrix<RES> m(packed + vq_books_bytes<RES>() + (size_t)ex[f] * expert_bytes + dn_off,
+                              (size_t)H, (size_t)I);
+#pragma unroll
+        for (int u = 0; u < TJ; ++u) m.load((size_t)rg * NJD + j0 + u, lane, cr[f][u][0]);
+    }
+
+    float acc[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        if (f > 0) {
+            lds_barrier();  // phase 0's readers are done with h16
+            stage_h16(1);
+            lds_barrier();
+        }
         float a1[1][2] = {{0.f, 0.f}};
 #pragma unroll
         for (int u = 0; u < TJ; ++u)
@@ -425,8 +438,8 @@ static hipError_t vd_gateup_launch(const Shape &s, const uint16_t *x, const uint
                                    const Workspace &ws, hipStream_t st) {
     const int grid = s.K * (s.I / 16) / kVdPairs;
     vq_dec_gateup<GW, TJ, NSL, RES><<<grid, kVdThreads, 0, st>>>(
-        x, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.logits, ws.idx, ws.w, ws.counts,
-        ws.offsets, ws.active, ws.perm, ws.inv, static_cast<float *>(ws.h),
+        x, ws.xexp, packed, s.expert_bytes, s.H, s.I, s.E, s.K, ws.logits, ws.idx, ws.w, ws.counts,
+        ws.offsets, ws.active, ws.perm, ws.inv, static_cast<float *>(ws.h), ws.hpmax,
         s.routing == MOE_ROUTE_SIGMOID);
     return hipGetLastError();
 }
@@ -455,7 +468,8 @@ static hipError_t vd_down_launch(const Shape &s, const uint8_t *packed, const Wo
                                  float *out, hipStream_t st) {
     vq_dec_down<TJ, RES><<<s.H / 16, kVdThreads, 0, st>>>(packed, s.expert_bytes, s.H, s.I, s.K,
                                                           ws.active, ws.perm, ws.w,
-                                                          static_cast<const float *>(ws.h), out);
+                                                          static_cast<const float *>(ws.h),
+                                                          ws.hpmax, out);
     return hipGetLastError();
 }
 
