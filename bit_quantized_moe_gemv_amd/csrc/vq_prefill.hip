@@ -476,16 +476,29 @@ __device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[kVgGroups][6], co
     vg_form_a<RES>(cbv, rbv, a);
 }
 
-// One pass (at most 128 tokens from route position pc) over the item's rows.
+// The index streams of one item's rows: the code12, plane and residual
+// regions of its matrix and the wave's row groups.
+struct VgCodes {
+    const uint8_t *c12, *pln, *res;
+    int grp[kVgGroups];
+};
+
+// One pass (at most 128 tokens from route position pc) over the item's rows
+// (codes cur).  cr holds the codes of two super-steps; with have_first the
+// previous pass already loaded this pass's super-step 0 into cr[0].  The code
+// loads of the last super-step fetch the next pass's super-step 0 (codes nxt,
+// when has_next) instead of repeating the last one, so no pass starts with a
+// wait on HBM for its first codes.
 template <int MODE, int MT, bool RES>
-__device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const uint8_t *pln,
-                                        const uint8_t *res, const uint16_t *gain,
-                                        const int (&grp)[kVgGroups], int NJ, int H, int I, int K,
-                                        int pc, int nt, int wave, int lane,
+__device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const uint16_t *gain,
+                                        const VgCodes &nxt, bool has_next, bool have_first,
+                                        uint32_t (&cr)[2][kVgGroups][6], int NJ, int H, int I,
+                                        int K, int pc, int nt, int wave, int lane,
                                         const int32_t *__restrict__ perm,
                                         const uint16_t *__restrict__ bsrc,
                                         const int32_t *__restrict__ bexp,
                                         float *__restrict__ out) {
+    const int(&grp)[kVgGroups] = cur.grp;
     const int q = lane >> 4, n = lane & 15;
     // An LDS slot holds one K step of 128 tokens ([piece q][token]) or, for
     // passes of at most 64 tokens, two K steps ([K step][piece q][token]):
@@ -506,15 +519,20 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t cr[2][kVgGroups][6];
+    // super-step J's codes into cr[slot]; past the last super-step they are
+    // the next pass's super-step 0 (or a repeat of the last one), chosen by
+    // uniform selects, so every call issues the same loads
     auto issue_codes = [&](int slot, int J) {
+        const bool to_next = J >= NJ && has_next;
+        const VgCodes &src = to_next ? nxt : cur;
+        const int Js = to_next ? 0 : min(J, NJ - 1);
 #pragma unroll
         for (int g = 0; g < kVgGroups; ++g) {
-            const size_t tile = (size_t)grp[g] * NJ + J;
-            const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
+            const size_t tile = (size_t)src.grp[g] * NJ + Js;
+            const u32x3 c = *reinterpret_cast<const u32x3 *>(src.c12 + tile * 768 + lane * 12);
             uint2 r = make_uint2(0u, 0u);
-            if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
-            const uint32_t p = pln[tile * 64 + lane];
+            if (RES) r = *reinterpret_cast<const uint2 *>(src.res + tile * 512 + lane * 8);
+            const uint32_t p = src.pln[tile * 64 + lane];
             cr[slot][g][0] = c.x;
             cr[slot][g][1] = c.y;
             cr[slot][g][2] = c.z;
@@ -539,8 +557,8 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
     constexpr int kCodeLoads = (RES ? 3 : 2) * kVgGroups;
 
     vq_stage_barrier();  // the previous pass's readers are done with the ring
-    const int NP = SPS * NJ, lastP = NP - 1, lastJ = NJ - 1;
-    issue_codes(0, 0);
+    const int NP = SPS * NJ, lastP = NP - 1;
+    if (!have_first) issue_codes(0, 0);
     load_b(0);
     vq_wait_vmcnt<0>();
     store_b(0);
@@ -570,7 +588,7 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const uint8_t *c12, const ui
                 store_b(min(P + 1, lastP));
                 vq_stage_barrier();
                 load_b(min(P + 2, lastP));
-                if (p == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
+                if (p == 0) issue_codes(jj ^ 1, J + 1);
                 if (J < NJ) {
 #pragma unroll
                     for (int kk = 0; kk < KPS; ++kk) {
@@ -666,38 +684,66 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
     const int stride = by_xcd ? (int)(gridDim.x >> 3) : (int)gridDim.x;
     const int items = by_xcd ? (E >> 3) * nslice : E * nslice;
 
-    for (int it = first; it < items; it += stride) {
+    // The block's passes in order: items it = first, first + stride, ...
+    // (empty experts skipped), chunks of kVgChunk tokens within an item.  Each
+    // pass is told the next one's index streams, whose first codes it loads.
+    struct Item {
+        int p0, ne;
+        const uint16_t *gain;
+        VgCodes codes;
+    };
+    auto item_at = [&](int it, Item &o) {  // false for an empty expert
         const int e = by_xcd ? xcd + 8 * (it / nslice) : it / nslice;
         const int slice = it % nslice;
-        const int p0 = offsets[e];
-        const int ne = offsets[e + 1] - p0;
-        if (ne == 0) continue;
+        o.p0 = offsets[e];
+        o.ne = offsets[e + 1] - o.p0;
         const uint8_t *mat = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
-        const uint8_t *c12 = mat;
-        const uint8_t *pln = c12 + nvec * 3 / 2;
-        const uint8_t *res = pln + nvec / 8;
-        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
-        int grp[kVgGroups];
+        o.codes.c12 = mat;
+        o.codes.pln = mat + nvec * 3 / 2;
+        o.codes.res = o.codes.pln + nvec / 8;
+        o.gain = reinterpret_cast<const uint16_t *>(o.codes.res + (RES ? nvec : 0));
         if (MODE == 0) {
-            grp[0] = 8 * slice + wave;          // gate group
-            grp[1] = I / 16 + 8 * slice + wave;  // its up partner
+            o.codes.grp[0] = 8 * slice + wave;          // gate group
+            o.codes.grp[1] = I / 16 + 8 * slice + wave;  // its up partner
         } else {
-            grp[0] = min(16 * slice + 2 * wave, H / 16 - 1);
-            grp[1] = min(16 * slice + 2 * wave + 1, H / 16 - 1);
+            o.codes.grp[0] = min(16 * slice + 2 * wave, H / 16 - 1);
+            o.codes.grp[1] = min(16 * slice + 2 * wave + 1, H / 16 - 1);
         }
-        for (int c0 = 0; c0 < ne; c0 += kVgChunk) {
-            const int nt = min(kVgChunk, ne - c0);
-            const int mt = (nt + 15) / 16;
-            auto pass = [&](auto mtc) {
-                vg_pass<MODE, decltype(mtc)::value, RES>(lds, c12, pln, res, gain, grp, NJ, H, I,
-                                                         K, p0 + c0, nt, wave, lane, perm, bsrc,
-                                                         bexp, out);
-            };
-            if (mt <= 2) pass(std::integral_constant<int, 2>{});
-            else if (mt <= 4) pass(std::integral_constant<int, 4>{});
-            else if (mt <= 6) pass(std::integral_constant<int, 6>{});
-            else pass(std::integral_constant<int, 8>{});
+        return o.ne > 0;
+    };
+    uint32_t cr[2][kVgGroups][6];
+    Item cur, nxt;
+    int it = first;
+    while (it < items && !item_at(it, cur)) it += stride;
+    int c0 = 0;
+    bool have_first = false;
+    while (it < items) {
+        int it2 = it, c2 = c0 + kVgChunk;
+        bool has_next = true;
+        if (c2 < cur.ne) {
+            nxt = cur;
+        } else {
+            c2 = 0;
+            it2 = it + stride;
+            while (it2 < items && !item_at(it2, nxt)) it2 += stride;
+            has_next = it2 < items;
+            if (!has_next) nxt = cur;
         }
+        const int nt = min(kVgChunk, cur.ne - c0);
+        const int mt = (nt + 15) / 16;
+        auto pass = [&](auto mtc) {
+            vg_pass<MODE, decltype(mtc)::value, RES>(lds, cur.codes, cur.gain, nxt.codes, has_next,
+                                                     have_first, cr, NJ, H, I, K, cur.p0 + c0, nt,
+                                                     wave, lane, perm, bsrc, bexp, out);
+        };
+        if (mt <= 2) pass(std::integral_constant<int, 2>{});
+        else if (mt <= 4) pass(std::integral_constant<int, 4>{});
+        else if (mt <= 6) pass(std::integral_constant<int, 6>{});
+        else pass(std::integral_constant<int, 8>{});
+        have_first = has_next;
+        it = it2;
+        c0 = c2;
+        cur = nxt;
     }
 }
 
