@@ -416,8 +416,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
 // up partners (wave w: gate group 8*slice + w and its up partner), B = x16
 // gathered through perm, out = h; MODE 1: slice = 256 output rows (wave w:
 // groups 16*slice + 2w, +1), B = h16 (route rows), out = y.  MT: the pass's
-// 16-token tiles, rounded up to even (a compile-time count, dispatched per
-// pass).  B goes through a 3-deep LDS ring of single K steps (4 pieces of 8
+// 16-token tiles (a compile-time count, dispatched per pass; a lone tile runs
+// as two).  B goes through a 3-deep LDS ring of single K steps (4 pieces of 8
 // columns x 128 tokens, 8 KiB); with both books that fills 156 KiB.
 // ---------------------------------------------------------------------------
 constexpr int kVgGroups = 2;
@@ -560,7 +560,22 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
     const int NP = SPS * NJ, lastP = NP - 1;
     if (!have_first) issue_codes(0, 0);
     load_b(0);
+    // The epilogue's operands travel with the first B rows: the gains of the
+    // wave's two groups (rows 4q..4q+3) and, per token tile, the exponent of
+    // the lane's token (MODE 0: through perm, so the exponent loads follow
+    // once perm has landed; the first step's full wait covers them).
+    const uint2 gw0 = *reinterpret_cast<const uint2 *>(gain + 16 * grp[0] + 4 * q);
+    const uint2 gw1 = *reinterpret_cast<const uint2 *>(gain + 16 * grp[1] + 4 * q);
+    int ex[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const int pt = pc + min(16 * t + n, nt - 1);
+        ex[t] = MODE == 0 ? perm[pt] : bexp[pt];
+    }
     vq_wait_vmcnt<0>();
+    if (MODE == 0)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) ex[t] = bexp[ex[t] / K];
     store_b(0);
     load_b(min(1, lastP));
     f16x8 a[kVgGroups];  // the A operands of the current K step
@@ -619,10 +634,9 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
         if (m >= nt) continue;
         const int p = pc + m;
         if (MODE == 0) {
-            const int xs = bexp[perm[p] / K];
-            const int gg = grp[0], ug = grp[1];
-            const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
-            const uint2 uw = *reinterpret_cast<const uint2 *>(gain + 16 * ug + 4 * q);
+            const int xs = ex[t];
+            const int gg = grp[0];
+            const uint2 gw = gw0, uw = gw1;
             const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
             const uint32_t ub[4] = {uw.x & 0xFFFFu, uw.x >> 16, uw.y & 0xFFFFu, uw.y >> 16};
             float hv[4];
@@ -635,13 +649,13 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
             *reinterpret_cast<float4 *>(out + (size_t)p * I + 16 * gg + 4 * q) =
                 make_float4(hv[0], hv[1], hv[2], hv[3]);
         } else {
-            const int hs = bexp[p];
+            const int hs = ex[t];
 #pragma unroll
             for (int g = 0; g < kVgGroups; ++g) {
                 const int gg = grp[g];
                 if (gg >= H / 16) continue;  // clamped duplicate past the last group
                 if (g == 1 && grp[1] == grp[0]) continue;
-                const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
+                const uint2 gw = g == 0 ? gw0 : gw1;
                 const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
                 float yv[4];
 #pragma unroll
@@ -736,10 +750,16 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
                                                      have_first, cr, NJ, H, I, K, cur.p0 + c0, nt,
                                                      wave, lane, perm, bsrc, bexp, out);
         };
-        if (mt <= 2) pass(std::integral_constant<int, 2>{});
-        else if (mt <= 4) pass(std::integral_constant<int, 4>{});
-        else if (mt <= 6) pass(std::integral_constant<int, 6>{});
-        else pass(std::integral_constant<int, 8>{});
+        switch (mt) {
+            case 1:
+            case 2: pass(std::integral_constant<int, 2>{}); break;
+            case 3: pass(std::integral_constant<int, 3>{}); break;
+            case 4: pass(std::integral_constant<int, 4>{}); break;
+            case 5: pass(std::integral_constant<int, 5>{}); break;
+            case 6: pass(std::integral_constant<int, 6>{}); break;
+            case 7: pass(std::integral_constant<int, 7>{}); break;
+            default: pass(std::integral_constant<int, 8>{}); break;
+        }
         have_first = has_next;
         it = it2;
         c0 = c2;
