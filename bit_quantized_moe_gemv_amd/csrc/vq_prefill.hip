@@ -25,8 +25,8 @@
 // 16-byte LDS reads per K step.  Batches of more than 16 tokens run
 // vq_grouped_kernel: an item covers 256 weight rows and all of the expert's
 // tokens, 128 per pass (up to 8 token tiles per gathered A fragment), with
-// the B operand streaming through a 3-deep LDS ring of single K steps (8
-// KiB each); batches of at most 16 tokens run vq_prefill_kernel over the
+// the B operand streaming through an LDS ring of two 14 KiB slots (two K
+// steps of up to 112 tokens each); batches of at most 16 tokens run vq_prefill_kernel over the
 // active experts only, one 16-token tile per MFMA, B in a ring of two-K-step
 // sub-steps.  The index streams of a 256-column super-step go straight to
 // registers one super-step ahead.
@@ -417,18 +417,21 @@ __global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
 // gathered through perm, out = h; MODE 1: slice = 256 output rows (wave w:
 // groups 16*slice + 2w, +1), B = h16 (route rows), out = y.  MT: the pass's
 // 16-token tiles (a compile-time count, dispatched per pass; a lone tile runs
-// as two).  B goes through a 3-deep LDS ring of single K steps (4 pieces of 8
-// columns x 128 tokens, 8 KiB); with both books that fills 156 KiB.
+// as two).  B goes through an LDS ring of two 14 KiB slots, each two K steps
+// of up to 112 tokens (4 pieces of 8 columns per K step and token) or one K
+// step of 128; with both books that fills the 160 KiB.
 // ---------------------------------------------------------------------------
 constexpr int kVgGroups = 2;
 constexpr int kVgChunk = 128;
-constexpr int kVgRing = 3;
+constexpr int kVgPair = 112;              // tokens of a two-K-step slot
+constexpr int kVgSlot = 2 * 4 * kVgPair;  // uint4 per slot: 14 KiB
 
 struct VgLds {
-    uint4 cb[kVqEntries];                  // 128 KiB
-    uint4 rb[kVqResEntries];               // 4 KiB
-    uint4 b[kVgRing][4][kVgChunk];         // [slot][q][token]: 8 columns of fp16
+    uint4 cb[kVqEntries];     // 128 KiB
+    uint4 rb[kVqResEntries];  // 4 KiB
+    uint4 b[2][kVgSlot];      // B ring: [K step][q][token] or [q][token], 8 fp16 each
 };
+static_assert(sizeof(VgLds) <= 160 * 1024, "the block's LDS");
 
 // Book rows of K step S for the wave's 2 groups (issued, not waited for).
 template <int S, bool RES>
@@ -500,19 +503,24 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
                                         float *__restrict__ out) {
     const int(&grp)[kVgGroups] = cur.grp;
     const int q = lane >> 4, n = lane & 15;
-    // An LDS slot holds one K step of 128 tokens ([piece q][token]) or, for
-    // passes of at most 64 tokens, two K steps ([K step][piece q][token]):
-    // then barriers come every two K steps.
-    constexpr int KPS = MT <= 4 ? 2 : 1;  // K steps per slot
-    constexpr int SPS = 8 / KPS;          // slot steps per super-step
+    // An LDS slot holds two K steps of up to 112 tokens ([K step][piece
+    // q][token]) or, for passes of more tokens, one K step of 128 ([q][token]),
+    // so most passes meet a barrier every two K steps.
+    constexpr int KPS = MT <= 7 ? 2 : 1;            // K steps per slot
+    constexpr int SPS = 8 / KPS;                    // slot steps per super-step
+    constexpr int NL = KPS == 2 && MT > 4 ? 2 : 1;  // B loads per lane and slot step
     // B staging: wave w moves piece w%4 (columns 64q + 8s..+7 of K step s) of
-    // tokens 64(w/4) + lane (one K step per slot) or of tokens lane, K step
-    // w/4 of the slot (two), one 16-byte register load per slot step
+    // K step w/4 of the slot for tokens lane and, with NL = 2, 64 + lane (two
+    // K steps per slot), or of tokens 64(w/4) + lane (one); 16-byte register
+    // loads, clamped to the pass's last token
     const int sq = wave & 3;
     const int kw = KPS == 2 ? wave >> 2 : 0;
-    const int tok = min((KPS == 2 ? 0 : 64 * (wave >> 2)) + lane, nt - 1);
-    const uint16_t *brow = MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H
-                                     : bsrc + (size_t)(pc + tok) * I;
+    auto token_row = [&](int tok) {
+        tok = min(tok, nt - 1);
+        return MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H : bsrc + (size_t)(pc + tok) * I;
+    };
+    const uint16_t *brow0 = token_row((KPS == 2 ? 0 : 64 * (wave >> 2)) + lane);
+    const uint16_t *brow1 = NL == 2 ? token_row(64 + lane) : brow0;
     f32x4 acc[kVgGroups][MT];
 #pragma unroll
     for (int g = 0; g < kVgGroups; ++g)
@@ -541,18 +549,26 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
             cr[slot][g][5] = p;
         }
     };
-    auto slot_base = [&](int P) { return &lds.b[P % kVgRing][0][0]; };
-    uint4 bstage;
+    auto slot_base = [&](int P) { return &lds.b[P & 1][0]; };
+    uint4 bst0, bst1;
     auto load_b = [&](int P) {  // slot step P; this wave's K step S = KPS*P + kw
         const int S = KPS * P + kw;
-        bstage = *reinterpret_cast<const uint4 *>(brow + 256 * (S >> 3) + 64 * sq + 8 * (S & 7));
+        const int off = 256 * (S >> 3) + 64 * sq + 8 * (S & 7);
+        bst0 = *reinterpret_cast<const uint4 *>(brow0 + off);
+        if constexpr (NL == 2) bst1 = *reinterpret_cast<const uint4 *>(brow1 + off);
     };
     auto store_b = [&](int P) {
-        slot_base(P)[KPS == 2 ? (kw * 4 + sq) * 64 + lane : sq * kVgChunk + 64 * (wave >> 2) + lane] =
-            bstage;
+        uint4 *base = slot_base(P);
+        if constexpr (KPS == 2) {
+            base[(kw * 4 + sq) * kVgPair + lane] = bst0;
+            if constexpr (NL == 2)
+                if (64 + lane < kVgPair) base[(kw * 4 + sq) * kVgPair + 64 + lane] = bst1;
+        } else {
+            base[sq * kVgChunk + 64 * (wave >> 2) + lane] = bst0;
+        }
     };
     auto b_row = [&](int P, int kk) -> const uint4 * {  // K step kk of slot step P, piece q
-        return slot_base(P) + (KPS == 2 ? (kk * 4 + q) * 64 : q * kVgChunk);
+        return slot_base(P) + (KPS == 2 ? (kk * 4 + q) * kVgPair : q * kVgChunk);
     };
     constexpr int kCodeLoads = (RES ? 3 : 2) * kVgGroups;
 
@@ -584,11 +600,13 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
         vg_gather<0, RES>(cr[0], lds, cbv, rbv);
         vg_form_a<RES>(cbv, rbv, a);
     }
-    // Per slot step P = SPS*J + p: B(P+1) (issued at P-1, followed by the code
-    // loads of super-step J+1 when P-1 began super-step J) lands and goes to
-    // LDS; the barrier publishes B(P); then B(P+2) and, at p = 0, the codes of
-    // super-step J+1 are issued.  Loads are issued every step (indices clamped
-    // past the end), so the wait counts are exact.
+    // Per slot step P = SPS*J + p: the barrier publishes B(P) (stored at P-1)
+    // and, every wave being done with step P-1, frees the other slot; B(P+1)
+    // (issued at P-1, followed by the code loads of super-step J+1 when P-1
+    // began super-step J) lands and goes there; then B(P+2) and, at p = 0, the
+    // codes of super-step J+1 are issued.  The loads stay in flight through
+    // the barrier.  Loads are issued every step (indices clamped past the
+    // end), so the wait counts are exact.
     for (int J0 = 0; J0 < NJ; J0 += 2) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -596,12 +614,12 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
 #pragma unroll
             for (int p = 0; p < SPS; ++p) {
                 const int P = SPS * J + p;
+                vq_stage_barrier();
                 if (p == 1)
                     vq_wait_vmcnt<kCodeLoads>();
                 else
                     vq_wait_vmcnt<0>();
                 store_b(min(P + 1, lastP));
-                vq_stage_barrier();
                 load_b(min(P + 2, lastP));
                 if (p == 0) issue_codes(jj ^ 1, J + 1);
                 if (J < NJ) {
