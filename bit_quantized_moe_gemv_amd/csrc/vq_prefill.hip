@@ -26,10 +26,11 @@
 // vq_grouped_kernel: an item covers 256 weight rows and all of the expert's
 // tokens, 128 per pass (up to 8 token tiles per gathered A fragment), with
 // the B operand streaming through an LDS ring of two 14 KiB slots (two K
-// steps of up to 112 tokens each); batches of at most 16 tokens run vq_prefill_kernel over the
-// active experts only, one 16-token tile per MFMA, B in a ring of two-K-step
-// sub-steps.  The index streams of a 256-column super-step go straight to
-// registers one super-step ahead.
+// steps of up to 112 tokens each), and the index streams of a 256-column
+// super-step going straight to registers one super-step ahead.  Batches of at
+// most 16 tokens run vq_small_kernel over the active experts only: one
+// 16-token tile per MFMA, index streams two super-steps ahead, B one
+// super-step per LDS slot.
 //
 // Lane roles.  A = 16 weight rows x 32 K of fp16 (lane l: row l%16, K slice
 // 8*(l/16)..+7).  In a VQ tile (16 rows x 256 columns) lane (n, q) owns the
@@ -45,14 +46,6 @@ namespace bqmoe {
 
 constexpr int kVqWaves = 8;  // two per SIMD, sharing the books
 constexpr int kVqThreads = kVqWaves * 64;
-constexpr int kVqGroups = 4;  // row groups (16 rows) per wave; 512 rows per block item
-constexpr int kVqRing = 3;    // B sub-stages in LDS
-
-struct VqLds {
-    uint4 cb[kVqEntries];     // 128 KiB
-    uint4 rb[kVqResEntries];  // 4 KiB
-    uint8_t b[kVqRing][2][4][64][16];  // [slot][K step parity][q][token][8 fp16]
-};
 
 template <int N>
 __device__ __forceinline__ void vq_wait_vmcnt() {
@@ -157,256 +150,6 @@ __global__ __launch_bounds__(256) void hpack_kernel(const float *__restrict__ h,
     }
 }
 
-// Book rows of K step S for one row group: Cb[i13] and (with the residual
-// stage) Rb[i8].  c[0..2] code12, c[3..4] res, c[5] plane byte.
-template <int S, bool RES>
-__device__ __forceinline__ void gather_a(const uint32_t (&c)[6], const VqLds &lds, uint4 &cbv,
-                                         uint4 &rbv) {
-    uint32_t i13, i8;
-    vq_indices<S>(c, i13, i8);
-    cbv = lds.cb[i13];
-    if (RES) rbv = lds.rb[i8];
-}
-
-// The A operand: Cb + Rb rounded once to fp16, or Cb alone.
-template <bool RES>
-__device__ __forceinline__ f16x8 a_operand(uint4 cbv, uint4 rbv) {
-    return RES ? add_f16x8(cbv, rbv) : __builtin_bit_cast(f16x8, cbv);
-}
-
-// One sub-step (two K steps) of a wave: 2 x 4 groups x NTT token tiles MFMAs.
-template <int U, int NTT, bool RES>
-__device__ __forceinline__ void vq_substep(const uint32_t (&cr)[kVqGroups][6], const VqLds &lds,
-                                           int slot, int lane, f32x4 (&acc)[kVqGroups][NTT]) {
-    const int q = lane >> 4, n = lane & 15;
-    uint4 cb0[kVqGroups], rb0[kVqGroups], cb1[kVqGroups], rb1[kVqGroups];
-    uint4 b0[NTT], b1[NTT];
-#pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U, RES>(cr[g], lds, cb0[g], rb0[g]);
-#pragma unroll
-    for (int t = 0; t < NTT; ++t)
-        b0[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][0][q][16 * t + n]);
-#pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) gather_a<2 * U + 1, RES>(cr[g], lds, cb1[g], rb1[g]);
-#pragma unroll
-    for (int t = 0; t < NTT; ++t)
-        b1[t] = *reinterpret_cast<const uint4 *>(lds.b[slot][1][q][16 * t + n]);
-    f16x8 a0[kVqGroups];
-#pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) a0[g] = a_operand<RES>(cb0[g], rb0[g]);
-#pragma unroll
-    for (int t = 0; t < NTT; ++t)
-#pragma unroll
-        for (int g = 0; g < kVqGroups; ++g)
-            acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                a0[g], __builtin_bit_cast(f16x8, b0[t]), acc[g][t], 0, 0, 0);
-    f16x8 a1[kVqGroups];
-#pragma unroll
-    for (int g = 0; g < kVqGroups; ++g) a1[g] = a_operand<RES>(cb1[g], rb1[g]);
-#pragma unroll
-    for (int t = 0; t < NTT; ++t)
-#pragma unroll
-        for (int g = 0; g < kVqGroups; ++g)
-            acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                a1[g], __builtin_bit_cast(f16x8, b1[t]), acc[g][t], 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// The grouped GEMM for batches of at most 16 tokens (so at most 16 routes per
-// expert).  MODE 0: gate/up + SwiGLU, B = x16 (gathered through perm), out =
-// h (fp32, [route position][I]).  MODE 1: down, B = h16 (route rows), out = y
-// (fp32, [route position][H]).  Item = (active expert, slice): MODE 0 slices
-// are 256 gate rows with their up partners (wave w: gate groups 16b+2w, +1
-// and the two up partners), MODE 1 slices are 512 output rows (wave w: groups
-// 32b+4w..+3, clamped past the end and never stored).  One 16-token tile per
-// MFMA (NTT = 1), and the items run over the active experts only (the list
-// the small-batch routing writes), so no MFMA works on absent tokens or
-// experts.  RES: the layer has the residual stage (VQ13R8) or not (VQ13).
-// ---------------------------------------------------------------------------
-template <int MODE, int NTT, bool RES>
-__global__ __launch_bounds__(kVqThreads) void vq_prefill_kernel(
-    const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int E,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ active, const uint16_t *__restrict__ bsrc,
-    const int32_t *__restrict__ bexp, float *__restrict__ out) {
-    static_assert(NTT == 1, "larger batches run vq_grouped_kernel");
-    constexpr int kChunk = 16;  // tokens per chunk: every routed expert of a small batch
-    __shared__ __align__(16) VqLds lds;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, q = lane >> 4;
-
-    {  // both books -> LDS, once per block
-        const uint4 *books = reinterpret_cast<const uint4 *>(packed);
-        for (int i = tid; i < kVqEntries; i += kVqThreads) lds.cb[i] = books[i];
-        if (RES)
-            for (int i = tid; i < kVqResEntries; i += kVqThreads) lds.rb[i] = books[kVqEntries + i];
-    }
-    __syncthreads();
-
-    const int NK = MODE == 0 ? H : I;        // reduction length
-    const int NROW = MODE == 0 ? 2 * I : H;  // matrix rows
-    const int NJ = NK / 256;                 // super-steps
-    const int NS = 4 * NJ;                   // sub-steps
-    const int nslice = MODE == 0 ? I / 256 : (H + 511) / 512;
-    const int per_e = nslice;
-    const size_t nvec = (size_t)NROW * NK / 8;
-    const size_t mat_off = MODE == 1 ? vq_down_offset((size_t)H, (size_t)I, RES) : 0;
-    constexpr int kCodeLoads = (RES ? 3 : 2) * kVqGroups;  // loads per wave per super-step
-
-    const int first = (int)blockIdx.x, stride = (int)gridDim.x;
-    const int items = active[0] * per_e;  // the active experts only
-
-    for (int it = first; it < items; it += stride) {
-        const int e = active[1 + it / per_e];
-        const int rest = it % per_e;
-        const int slice = rest;
-        const int p0 = offsets[e];
-        const int ne = offsets[e + 1] - p0;
-        const uint8_t *mat = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
-        const uint8_t *c12 = mat;
-        const uint8_t *pln = c12 + nvec * 3 / 2;
-        const uint8_t *res = pln + nvec / 8;
-        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
-
-        int grp[kVqGroups];
-#pragma unroll
-        for (int g = 0; g < kVqGroups; ++g) {
-            if (MODE == 0)
-                grp[g] = (g < 2 ? 0 : I / 16) + 16 * slice + 2 * wave + (g & 1);
-            else
-                grp[g] = min(32 * slice + 4 * wave + g, H / 16 - 1);
-        }
-
-        for (int c0 = 0; c0 < ne; c0 += kChunk) {
-            const int nt = min(kChunk, ne - c0);
-            const int pr = p0 + c0 + min(lane, nt - 1);
-            const uint16_t *brow =
-                MODE == 0 ? bsrc + (size_t)(perm[pr] / K) * H : bsrc + (size_t)pr * I;
-
-            f32x4 acc[kVqGroups][NTT];
-#pragma unroll
-            for (int g = 0; g < kVqGroups; ++g)
-#pragma unroll
-                for (int t = 0; t < NTT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-            uint32_t cr[2][kVqGroups][6];
-            auto issue_codes = [&](int slot, int J) {
-#pragma unroll
-                for (int g = 0; g < kVqGroups; ++g) {
-                    const size_t tile = (size_t)grp[g] * NJ + J;
-                    const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
-                    uint2 r = make_uint2(0u, 0u);
-                    if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
-                    const uint32_t p = pln[tile * 64 + lane];
-                    cr[slot][g][0] = c.x;
-                    cr[slot][g][1] = c.y;
-                    cr[slot][g][2] = c.z;
-                    cr[slot][g][3] = r.x;
-                    cr[slot][g][4] = r.y;
-                    cr[slot][g][5] = p;
-                }
-            };
-            // Wave w stages the (K step parity w/4, q = w%4) 1 KiB piece of each
-            // sub-step: a 16-byte register load per lane, written to the LDS ring
-            // one sub-step later.  (Register staging instead of global_load_lds:
-            // the compiler cannot tell an LDS DMA target from the books and would
-            // wait for every such copy in flight before each LDS read.)
-            uint4 bstage;
-            auto load_b = [&](int S) {
-                const int J = S >> 2, u = S & 3, sb = wave >> 2, qq = wave & 3;
-                bstage = *reinterpret_cast<const uint4 *>(brow + 256 * J + 64 * qq + 16 * u + 8 * sb);
-            };
-            auto store_b = [&](int S) {
-                const int sb = wave >> 2, qq = wave & 3;
-                *reinterpret_cast<uint4 *>(lds.b[S % kVqRing][sb][qq][lane]) = bstage;
-            };
-
-            vq_stage_barrier();  // the previous chunk's readers are done with the ring
-            const int lastS = NS - 1, lastJ = NJ - 1;
-            issue_codes(0, 0);
-            load_b(0);
-            vq_wait_vmcnt<0>();
-            store_b(0);
-            load_b(min(1, lastS));
-            // Per sub-step S = 4J+u: the load of B(S+1) (issued at S-1, followed
-            // by the 12 code loads when S-1 began a super-step) lands and goes to
-            // LDS; the barrier publishes B(S); then B(S+2) and, at u = 0, the
-            // codes of super-step J+1 are issued.  Loads are issued every step
-            // (indices clamped past the end), so the wait counts are exact.
-            for (int J0 = 0; J0 < NJ; J0 += 2) {
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int J = J0 + jj;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int S = 4 * J + u;
-                        if (u == 1)
-                            vq_wait_vmcnt<kCodeLoads>();
-                        else
-                            vq_wait_vmcnt<0>();
-                        store_b(min(S + 1, lastS));
-                        vq_stage_barrier();
-                        load_b(min(S + 2, lastS));
-                        if (u == 0) issue_codes(jj ^ 1, min(J + 1, lastJ));
-                        if (J < NJ) {
-                            const int slot = S % kVqRing;
-                            if (u == 0) vq_substep<0, NTT, RES>(cr[jj], lds, slot, lane, acc);
-                            if (u == 1) vq_substep<1, NTT, RES>(cr[jj], lds, slot, lane, acc);
-                            if (u == 2) vq_substep<2, NTT, RES>(cr[jj], lds, slot, lane, acc);
-                            if (u == 3) vq_substep<3, NTT, RES>(cr[jj], lds, slot, lane, acc);
-                        }
-                    }
-                }
-            }
-            vq_wait_vmcnt<0>();  // the repeated tail loads land before the ring is reused
-
-            // epilogue: lane holds rows 4q..4q+3 of each group for token 16t+n
-#pragma unroll
-            for (int t = 0; t < NTT; ++t) {
-                const int m = 16 * t + n;
-                if (m >= nt) continue;
-                const int p = p0 + c0 + m;
-                if (MODE == 0) {
-                    const int xs = bexp[perm[p] / K];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const int gg = grp[i], ug = grp[2 + i];
-                        const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
-                        const uint2 uw = *reinterpret_cast<const uint2 *>(gain + 16 * ug + 4 * q);
-                        const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
-                        const uint32_t ub[4] = {uw.x & 0xFFFFu, uw.x >> 16, uw.y & 0xFFFFu, uw.y >> 16};
-                        float hv[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float gv = ldexpf(acc[i][t][j] * f16_bits_to_f32(gb[j]), xs);
-                            const float uv = ldexpf(acc[2 + i][t][j] * f16_bits_to_f32(ub[j]), xs);
-                            hv[j] = silu_f32(gv) * uv;
-                        }
-                        *reinterpret_cast<float4 *>(out + (size_t)p * I + 16 * gg + 4 * q) =
-                            make_float4(hv[0], hv[1], hv[2], hv[3]);
-                    }
-                } else {
-                    const int hs = bexp[p];
-#pragma unroll
-                    for (int g = 0; g < kVqGroups; ++g) {
-                        const int gg = 32 * slice + 4 * wave + g;
-                        if (gg >= H / 16) continue;
-                        const uint2 gw = *reinterpret_cast<const uint2 *>(gain + 16 * gg + 4 * q);
-                        const uint32_t gb[4] = {gw.x & 0xFFFFu, gw.x >> 16, gw.y & 0xFFFFu, gw.y >> 16};
-                        float yv[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            yv[j] = ldexpf(acc[g][t][j] * f16_bits_to_f32(gb[j]), hs);
-                        *reinterpret_cast<float4 *>(out + (size_t)p * H + 16 * gg + 4 * q) =
-                            make_float4(yv[0], yv[1], yv[2], yv[3]);
-                    }
-                }
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // The grouped GEMM for batches of more than 16 tokens.  Item = (expert,
 // slice); a block covers 256 weight rows of its slice (wave w: row groups
@@ -433,12 +176,12 @@ struct VgLds {
 };
 static_assert(sizeof(VgLds) <= 160 * 1024, "the block's LDS");
 
-// Book rows of K step S for the wave's 2 groups (issued, not waited for).
-template <int S, bool RES>
-__device__ __forceinline__ void vg_gather(const uint32_t (&cr)[kVgGroups][6], const VgLds &lds,
-                                          uint4 (&cbv)[kVgGroups], uint4 (&rbv)[kVgGroups]) {
+// Book rows of K step S for the wave's G groups (issued, not waited for).
+template <int S, bool RES, int G, class L>
+__device__ __forceinline__ void vg_gather(const uint32_t (&cr)[G][6], const L &lds, uint4 (&cbv)[G],
+                                          uint4 (&rbv)[G]) {
 #pragma unroll
-    for (int g = 0; g < kVgGroups; ++g) {
+    for (int g = 0; g < G; ++g) {
         uint32_t i13, i8;
         vq_indices<S>(cr[g], i13, i8);
         cbv[g] = lds.cb[i13];
@@ -446,34 +189,33 @@ __device__ __forceinline__ void vg_gather(const uint32_t (&cr)[kVgGroups][6], co
     }
 }
 
-template <bool RES>
-__device__ __forceinline__ void vg_form_a(const uint4 (&cbv)[kVgGroups],
-                                          const uint4 (&rbv)[kVgGroups], f16x8 (&a)[kVgGroups]) {
+template <bool RES, int G>
+__device__ __forceinline__ void vg_form_a(const uint4 (&cbv)[G], const uint4 (&rbv)[G],
+                                          f16x8 (&a)[G]) {
 #pragma unroll
-    for (int g = 0; g < kVgGroups; ++g)
+    for (int g = 0; g < G; ++g)
         a[g] = RES ? add_f16x8(cbv[g], rbv[g]) : __builtin_bit_cast(f16x8, cbv[g]);
 }
 
-// One K step of a wave: 2 groups x MT token tiles with the A operands a
+// One K step of a wave: G groups x MT token tiles with the A operands a
 // (gathered one K step earlier) and B from the LDS row bq (the step's piece
 // q = lane/16, indexed by token).  The step's B reads go first, then the book
 // gathers of the next K step SN (codes crn), then the MFMAs, which wait for
 // the B reads only (LDS reads complete in order), so the gathers' latency
 // hides under the MFMAs; a then becomes the next step's A.
-template <int SN, int MT, bool RES>
-__device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[kVgGroups][6], const VgLds &lds,
-                                         const uint4 *bq, int lane, f16x8 (&a)[kVgGroups],
-                                         f32x4 (&acc)[kVgGroups][MT]) {
+template <int SN, int MT, bool RES, int G, class L>
+__device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[G][6], const L &lds, const uint4 *bq,
+                                         int lane, f16x8 (&a)[G], f32x4 (&acc)[G][MT]) {
     const int n = lane & 15;
     uint4 bv[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) bv[t] = bq[16 * t + n];  // token 16t + n of the lane's piece
-    uint4 cbv[kVgGroups], rbv[kVgGroups];
+    uint4 cbv[G], rbv[G];
     vg_gather<SN, RES>(crn, lds, cbv, rbv);
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int g = 0; g < kVgGroups; ++g)
+        for (int g = 0; g < G; ++g)
             acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], __builtin_bit_cast(f16x8, bv[t]),
                                                                acc[g][t], 0, 0, 0);
     vg_form_a<RES>(cbv, rbv, a);
@@ -785,20 +527,204 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batches of at most 16 tokens (so at most 16 routes per expert), over the
+// active experts that the small-batch routing lists.  Each wave owns G row
+// groups: 4 for VQ13 layers, 2 with the residual stage (whose index streams
+// and gathers would not fit in registers for 4).  Item = (active expert,
+// slice): MODE 0 slice = 64G gate rows and their up partners (wave w: gate
+// groups (G/2)(8*slice + w) + i, i < G/2, and their up partners), MODE 1 slice
+// = 128G output rows (wave w: groups G(8*slice + w) + g, clamped past the end
+// and never stored).  One 16-token tile, so the index streams carry the kernel:
+// they go to registers two super-steps ahead (a ring of three), and B, one
+// super-step of 16 tokens (8 KiB), goes through two LDS slots, so a pass
+// meets one barrier per super-step.  The K steps run as in the grouped GEMM
+// (the next step's book rows gathered under the current step's MFMAs).
+// ---------------------------------------------------------------------------
+template <bool RES>
+constexpr int vs_groups() { return RES ? 2 : 4; }
+
+struct VsLds {
+    uint4 cb[kVqEntries];     // 128 KiB
+    uint4 rb[kVqResEntries];  // 4 KiB
+    uint4 b[2][8][4][16];     // [slot][K step][piece q][token]: 8 fp16 each
+};
+
+template <int MODE, bool RES>
+__global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
+    const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ active, const uint16_t *__restrict__ bsrc,
+    const int32_t *__restrict__ bexp, float *__restrict__ out) {
+    constexpr int G = vs_groups<RES>();
+    constexpr int GG = G / 2;  // gate groups per wave (MODE 0)
+    __shared__ __align__(16) VsLds lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    {  // both books -> LDS, once per block
+        const uint4 *books = reinterpret_cast<const uint4 *>(packed);
+        for (int i = tid; i < kVqEntries; i += kVqThreads) lds.cb[i] = books[i];
+        if (RES)
+            for (int i = tid; i < kVqResEntries; i += kVqThreads) lds.rb[i] = books[kVqEntries + i];
+    }
+    __syncthreads();
+
+    const int NK = MODE == 0 ? H : I;        // reduction length
+    const int NROW = MODE == 0 ? 2 * I : H;  // matrix rows
+    const int NJ = NK / 256;                 // super-steps
+    const int nslice = MODE == 0 ? I / (128 * GG) : (H + 128 * G - 1) / (128 * G);
+    const size_t nvec = (size_t)NROW * NK / 8;
+    const size_t mat_off = MODE == 1 ? vq_down_offset((size_t)H, (size_t)I, RES) : 0;
+    constexpr int kCodeLoads = (RES ? 3 : 2) * G;  // loads per wave per super-step
+    const int items = active[0] * nslice;
+
+    for (int it = (int)blockIdx.x; it < items; it += (int)gridDim.x) {
+        const int e = active[1 + it / nslice];
+        const int slice = it % nslice;
+        const int p0 = offsets[e];
+        const int ne = offsets[e + 1] - p0;
+        const uint8_t *c12 = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
+        const uint8_t *pln = c12 + nvec * 3 / 2;
+        const uint8_t *res = pln + nvec / 8;
+        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
+        int grp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            grp[g] = MODE == 0 ? (g < GG ? 0 : I / 16) + GG * (8 * slice + wave) + g % GG
+                               : min(G * (8 * slice + wave) + g, H / 16 - 1);
+
+        for (int c0 = 0; c0 < ne; c0 += 16) {
+            const int nt = min(16, ne - c0);
+            const int pc = p0 + c0;
+            // lane (n, q) stages piece q of token n (clamped to the pass) for
+            // K step `wave` of each super-step, and its epilogue covers token n
+            const int tok = min(n, nt - 1);
+            const uint16_t *brow = MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H
+                                             : bsrc + (size_t)(pc + tok) * I;
+            uint32_t cr[3][G][6];  // super-step J's codes in cr[J % 3]
+            auto issue_codes = [&](int slot, int J) {  // past the end: the last super-step again
+                J = min(J, NJ - 1);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const size_t tile = (size_t)grp[g] * NJ + J;
+                    const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
+                    uint2 r = make_uint2(0u, 0u);
+                    if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
+                    const uint32_t pb = pln[tile * 64 + lane];
+                    cr[slot][g][0] = c.x;
+                    cr[slot][g][1] = c.y;
+                    cr[slot][g][2] = c.z;
+                    cr[slot][g][3] = r.x;
+                    cr[slot][g][4] = r.y;
+                    cr[slot][g][5] = pb;
+                }
+            };
+            uint4 bst;
+            auto load_b = [&](int J) {
+                bst = *reinterpret_cast<const uint4 *>(brow + 256 * min(J, NJ - 1) + 64 * q + 8 * wave);
+            };
+            auto store_b = [&](int J) { lds.b[J & 1][wave][q][n] = bst; };
+            f32x4 acc[G][1];
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            vq_stage_barrier();  // the previous pass's readers are done with the ring
+            issue_codes(0, 0);
+            issue_codes(1, 1);
+            load_b(0);
+            // the epilogue's operands: the groups' gains (rows 4q..4q+3) and
+            // the exponent of token n (MODE 0: through perm)
+            uint2 gw[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                gw[g] = *reinterpret_cast<const uint2 *>(gain + 16 * grp[g] + 4 * q);
+            int ex = MODE == 0 ? perm[pc + tok] : bexp[pc + tok];
+            vq_wait_vmcnt<0>();
+            if (MODE == 0) ex = bexp[ex / K];
+            store_b(0);
+            load_b(1);
+            f16x8 a[G];  // the A operands of the current K step
+            {
+                uint4 cbv[G], rbv[G];
+                vg_gather<0, RES>(cr[0], lds, cbv, rbv);
+                vg_form_a<RES>(cbv, rbv, a);
+            }
+            // Per super-step J: the barrier publishes B(J) (stored at J-1) and,
+            // every wave being done with step J-1, frees the other slot; B(J+1)
+            // (issued at J-1, ahead of the codes of J+1) lands and goes there;
+            // then B(J+2) and the codes of J+2 are issued.  The codes of J+1
+            // are first needed by the gathers of the step's last K step.
+            for (int J0 = 0; J0 < NJ; J0 += 3) {
+#pragma unroll
+                for (int jj = 0; jj < 3; ++jj) {
+                    const int J = J0 + jj;
+                    vq_stage_barrier();
+                    vq_wait_vmcnt<kCodeLoads>();
+                    store_b(J + 1);
+                    load_b(J + 2);
+                    issue_codes((jj + 2) % 3, J + 2);
+                    if (J < NJ) {
+                        const uint4 *bs = &lds.b[J & 1][0][q][0];  // K step s at bs + 64 s
+                        const uint32_t(&c)[G][6] = cr[jj];
+                        vg_kstep<1, 1, RES>(c, lds, bs, lane, a, acc);
+                        vg_kstep<2, 1, RES>(c, lds, bs + 64, lane, a, acc);
+                        vg_kstep<3, 1, RES>(c, lds, bs + 128, lane, a, acc);
+                        vg_kstep<4, 1, RES>(c, lds, bs + 192, lane, a, acc);
+                        vg_kstep<5, 1, RES>(c, lds, bs + 256, lane, a, acc);
+                        vg_kstep<6, 1, RES>(c, lds, bs + 320, lane, a, acc);
+                        vg_kstep<7, 1, RES>(c, lds, bs + 384, lane, a, acc);
+                        vg_kstep<0, 1, RES>(cr[(jj + 1) % 3], lds, bs + 448, lane, a, acc);
+                    }
+                }
+            }
+            vq_wait_vmcnt<0>();  // the repeated tail loads land before the ring is reused
+
+            // epilogue: lane holds rows 4q..4q+3 of each group for token n
+            if (n < nt) {
+                const int p = pc + n;
+                if (MODE == 0) {
+#pragma unroll
+                    for (int i = 0; i < GG; ++i) {
+                        const uint2 g2 = gw[i], u2 = gw[GG + i];
+                        const uint32_t gb[4] = {g2.x & 0xFFFFu, g2.x >> 16, g2.y & 0xFFFFu, g2.y >> 16};
+                        const uint32_t ub[4] = {u2.x & 0xFFFFu, u2.x >> 16, u2.y & 0xFFFFu, u2.y >> 16};
+                        float hv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float gv = ldexpf(acc[i][0][j] * f16_bits_to_f32(gb[j]), ex);
+                            const float uv = ldexpf(acc[GG + i][0][j] * f16_bits_to_f32(ub[j]), ex);
+                            hv[j] = silu_f32(gv) * uv;
+                        }
+                        *reinterpret_cast<float4 *>(out + (size_t)p * I + 16 * grp[i] + 4 * q) =
+                            make_float4(hv[0], hv[1], hv[2], hv[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int gg = G * (8 * slice + wave) + g;
+                        if (gg >= H / 16) continue;  // clamped duplicate past the last group
+                        const uint2 g2 = gw[g];
+                        const uint32_t gb[4] = {g2.x & 0xFFFFu, g2.x >> 16, g2.y & 0xFFFFu, g2.y >> 16};
+                        float yv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            yv[j] = ldexpf(acc[g][0][j] * f16_bits_to_f32(gb[j]), ex);
+                        *reinterpret_cast<float4 *>(out + (size_t)p * H + 16 * gg + 4 * q) =
+                            make_float4(yv[0], yv[1], yv[2], yv[3]);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Persistent grid: one block per CU (the books fill most of the LDS), a
 // multiple of 8 when there is enough work so every XCD gets the same share.
 static int vq_grid(int items) {
     int g = min(items, device_cu_count());
     if (g >= 8) g &= ~7;
     return max(g, 1);
-}
-
-template <int MODE, int NTT, bool RES>
-static void vq_launch3(const Shape &s, int items, const uint8_t *packed, const Workspace &ws,
-                       const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
-    vq_prefill_kernel<MODE, NTT, RES><<<vq_grid(items), kVqThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, ws.active, bsrc, bexp,
-        out);
 }
 
 template <int MODE>
@@ -814,13 +740,23 @@ static void vg_launch(const Shape &s, const uint8_t *packed, const Workspace &ws
             packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out);
 }
 
-template <int MODE, int NTT>
-static void vq_launch(const Shape &s, int items, const uint8_t *packed, const Workspace &ws,
+// items: at most min(T*K, E) active experts times the slices per expert
+template <int MODE, bool RES>
+static void vs_launch(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
+                      const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
+    constexpr int G = vs_groups<RES>();
+    const int ns = MODE == 0 ? s.I / (64 * G) : (s.H + 128 * G - 1) / (128 * G);
+    vq_small_kernel<MODE, RES><<<vq_grid(min(T * s.K, s.E) * ns), kVqThreads, 0, st>>>(
+        packed, s.expert_bytes, s.H, s.I, s.K, ws.offsets, ws.perm, ws.active, bsrc, bexp, out);
+}
+
+template <int MODE>
+static void vs_launch(const Shape &s, int T, const uint8_t *packed, const Workspace &ws,
                       const uint16_t *bsrc, const int32_t *bexp, float *out, hipStream_t st) {
     if (s.fmt == MOE_FMT_VQ13R8)
-        vq_launch3<MODE, NTT, true>(s, items, packed, ws, bsrc, bexp, out, st);
+        vs_launch<MODE, true>(s, T, packed, ws, bsrc, bexp, out, st);
     else
-        vq_launch3<MODE, NTT, false>(s, items, packed, ws, bsrc, bexp, out, st);
+        vs_launch<MODE, false>(s, T, packed, ws, bsrc, bexp, out, st);
 }
 
 hipError_t launch_hpack(const Shape &s, int R, const Workspace &ws, hipStream_t st) {
@@ -837,16 +773,15 @@ hipError_t launch_hpack(const Shape &s, int R, const Workspace &ws, hipStream_t 
 }
 
 // Batches of at most kDecodeMaxTokens tokens (routed by the small-batch
-// routing, which lists the active experts) take the one-tile variant.
+// routing, which lists the active experts) take vq_small_kernel.
 hipError_t launch_vq_prefill_gateup(const Shape &s, int T, const uint16_t *x,
                                     const uint8_t *packed, const Workspace &ws, hipStream_t st) {
     vq_xpack_kernel<<<T, 256, 0, st>>>(x, s.H, ws.x16, ws.xexp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int ns = s.I / 256;
     float *h = static_cast<float *>(ws.h);
     if (T <= kDecodeMaxTokens)
-        vq_launch<0, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.x16, ws.xexp, h, st);
+        vs_launch<0>(s, T, packed, ws, ws.x16, ws.xexp, h, st);
     else
         vg_launch<0>(s, packed, ws, ws.x16, ws.xexp, h, st);
     return hipGetLastError();
@@ -856,9 +791,8 @@ hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
                                   const Workspace &ws, hipStream_t st) {
     hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
-    const int ns = (s.H + 511) / 512;
     if (T <= kDecodeMaxTokens)
-        vq_launch<1, 1>(s, min(T * s.K, s.E) * ns, packed, ws, ws.h16, ws.hexp, ws.y, st);
+        vs_launch<1>(s, T, packed, ws, ws.h16, ws.hexp, ws.y, st);
     else
         vg_launch<1>(s, packed, ws, ws.h16, ws.hexp, ws.y, st);
     return hipGetLastError();
