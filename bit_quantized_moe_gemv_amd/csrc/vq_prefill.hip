@@ -579,39 +579,77 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
     constexpr int kCodeLoads = (RES ? 3 : 2) * G;  // loads per wave per super-step
     const int items = active[0] * nslice;
 
-    for (int it = (int)blockIdx.x; it < items; it += (int)gridDim.x) {
+    // The block's passes in order: items it = blockIdx.x, +gridDim.x, ...
+    // (every listed expert has tokens), chunks of 16 tokens within an item.
+    struct Item {
+        int p0, ne, slice;
+        const uint16_t *gain;
+        const uint8_t *c12, *pln, *res;
+        int grp[G];
+    };
+    auto item_at = [&](int it, Item &o) {
         const int e = active[1 + it / nslice];
         const int slice = it % nslice;
-        const int p0 = offsets[e];
-        const int ne = offsets[e + 1] - p0;
-        const uint8_t *c12 = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
-        const uint8_t *pln = c12 + nvec * 3 / 2;
-        const uint8_t *res = pln + nvec / 8;
-        const uint16_t *gain = reinterpret_cast<const uint16_t *>(res + (RES ? nvec : 0));
-        int grp[G];
+        o.slice = slice;
+        o.p0 = offsets[e];
+        o.ne = offsets[e + 1] - o.p0;
+        o.c12 = packed + vq_books_bytes<RES>() + (size_t)e * expert_bytes + mat_off;
+        o.pln = o.c12 + nvec * 3 / 2;
+        o.res = o.pln + nvec / 8;
+        o.gain = reinterpret_cast<const uint16_t *>(o.res + (RES ? nvec : 0));
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            grp[g] = MODE == 0 ? (g < GG ? 0 : I / 16) + GG * (8 * slice + wave) + g % GG
-                               : min(G * (8 * slice + wave) + g, H / 16 - 1);
-
-        for (int c0 = 0; c0 < ne; c0 += 16) {
-            const int nt = min(16, ne - c0);
-            const int pc = p0 + c0;
+            o.grp[g] = MODE == 0 ? (g < GG ? 0 : I / 16) + GG * (8 * slice + wave) + g % GG
+                                 : min(G * (8 * slice + wave) + g, H / 16 - 1);
+    };
+    // super-step J's codes sit in cr[J % 4]; when NJ is a multiple of 4 the
+    // last two super-steps of a pass load the next pass's first two into
+    // slots 0 and 1
+    const bool chain = (NJ & 3) == 0;
+    uint32_t cr[4][G][6];
+    int it = (int)blockIdx.x;
+    if (it >= items) return;
+    Item cur, nxt;
+    item_at(it, cur);
+    int c0 = 0;
+    bool have_first = false;
+    while (true) {
+        int it2 = it, c2 = c0 + 16;
+        bool has_next = true;
+        if (c2 < cur.ne) {
+            nxt = cur;
+        } else {
+            c2 = 0;
+            it2 = it + (int)gridDim.x;
+            has_next = it2 < items;
+            if (has_next) item_at(it2, nxt);
+            else nxt = cur;
+        }
+        const bool pf = has_next && chain;
+        {
+            const int(&grp)[G] = cur.grp;
+            const uint16_t *gain = cur.gain;
+            const int nt = min(16, cur.ne - c0);
+            const int pc = cur.p0 + c0;
             // lane (n, q) stages piece q of token n (clamped to the pass) for
             // K step `wave` of each super-step, and its epilogue covers token n
             const int tok = min(n, nt - 1);
             const uint16_t *brow = MODE == 0 ? bsrc + (size_t)(perm[pc + tok] / K) * H
                                              : bsrc + (size_t)(pc + tok) * I;
-            uint32_t cr[3][G][6];  // super-step J's codes in cr[J % 3]
-            auto issue_codes = [&](int slot, int J) {  // past the end: the last super-step again
-                J = min(J, NJ - 1);
+            // super-step J's codes into cr[slot]; past the last super-step
+            // they are the next pass's (with pf) or the last one again, chosen
+            // by uniform selects, so every call issues the same loads
+            auto issue_codes = [&](int slot, int J) {
+                const bool to_next = J >= NJ && pf;
+                const Item &src = to_next ? nxt : cur;
+                const int Js = to_next ? J - NJ : min(J, NJ - 1);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const size_t tile = (size_t)grp[g] * NJ + J;
-                    const u32x3 c = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
+                    const size_t tile = (size_t)src.grp[g] * NJ + Js;
+                    const u32x3 c = *reinterpret_cast<const u32x3 *>(src.c12 + tile * 768 + lane * 12);
                     uint2 r = make_uint2(0u, 0u);
-                    if (RES) r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
-                    const uint32_t pb = pln[tile * 64 + lane];
+                    if (RES) r = *reinterpret_cast<const uint2 *>(src.res + tile * 512 + lane * 8);
+                    const uint32_t pb = src.pln[tile * 64 + lane];
                     cr[slot][g][0] = c.x;
                     cr[slot][g][1] = c.y;
                     cr[slot][g][2] = c.z;
@@ -630,8 +668,10 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
             for (int g = 0; g < G; ++g) acc[g][0] = f32x4{0.f, 0.f, 0.f, 0.f};
 
             vq_stage_barrier();  // the previous pass's readers are done with the ring
-            issue_codes(0, 0);
-            issue_codes(1, 1);
+            if (!have_first) {
+                issue_codes(0, 0);
+                issue_codes(1, 1);
+            }
             load_b(0);
             // the epilogue's operands: the groups' gains (rows 4q..4q+3) and
             // the exponent of token n (MODE 0: through perm)
@@ -655,15 +695,15 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
             // (issued at J-1, ahead of the codes of J+1) lands and goes there;
             // then B(J+2) and the codes of J+2 are issued.  The codes of J+1
             // are first needed by the gathers of the step's last K step.
-            for (int J0 = 0; J0 < NJ; J0 += 3) {
+            for (int J0 = 0; J0 < NJ; J0 += 4) {
 #pragma unroll
-                for (int jj = 0; jj < 3; ++jj) {
+                for (int jj = 0; jj < 4; ++jj) {
                     const int J = J0 + jj;
                     vq_stage_barrier();
                     vq_wait_vmcnt<kCodeLoads>();
                     store_b(J + 1);
                     load_b(J + 2);
-                    issue_codes((jj + 2) % 3, J + 2);
+                    issue_codes((jj + 2) & 3, J + 2);
                     if (J < NJ) {
                         const uint4 *bs = &lds.b[J & 1][0][q][0];  // K step s at bs + 64 s
                         const uint32_t(&c)[G][6] = cr[jj];
@@ -674,11 +714,13 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
                         vg_kstep<5, 1, RES>(c, lds, bs + 256, lane, a, acc);
                         vg_kstep<6, 1, RES>(c, lds, bs + 320, lane, a, acc);
                         vg_kstep<7, 1, RES>(c, lds, bs + 384, lane, a, acc);
-                        vg_kstep<0, 1, RES>(cr[(jj + 1) % 3], lds, bs + 448, lane, a, acc);
+                        vg_kstep<0, 1, RES>(cr[(jj + 1) & 3], lds, bs + 448, lane, a, acc);
                     }
                 }
             }
-            vq_wait_vmcnt<0>();  // the repeated tail loads land before the ring is reused
+            // the B loads past the end have landed; the codes issued last (the
+            // next pass's, with pf) may stay in flight through the epilogue
+            vq_wait_vmcnt<kCodeLoads>();
 
             // epilogue: lane holds rows 4q..4q+3 of each group for token n
             if (n < nt) {
@@ -702,7 +744,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
                 } else {
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const int gg = G * (8 * slice + wave) + g;
+                        const int gg = G * (8 * cur.slice + wave) + g;
                         if (gg >= H / 16) continue;  // clamped duplicate past the last group
                         const uint2 g2 = gw[g];
                         const uint32_t gb[4] = {g2.x & 0xFFFFu, g2.x >> 16, g2.y & 0xFFFFu, g2.y >> 16};
@@ -716,6 +758,11 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
                 }
             }
         }
+        if (!has_next) break;
+        have_first = pf;
+        it = it2;
+        c0 = c2;
+        cur = nxt;
     }
 }
 
