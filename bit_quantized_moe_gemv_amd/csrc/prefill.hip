@@ -325,17 +325,20 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
     int H, int I, int K, int E, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, float *__restrict__ h) {
     __shared__ __align__(16) GuLds lds;
-    int e, b;
-    map_expert_block(blockIdx.x, E, I / 128, &e, &b);
-    const int p0 = offsets[e];
-    const int ne = offsets[e + 1] - p0;
-    if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
     const int ngate = I / 16;
-    const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const size_t kt = (size_t)(H / 32);
+    const int nitems = E * (I / 128);
+    bool first = true;
+    for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
+    int e, b;
+    map_expert_block(item, E, I / 128, &e, &b);
+    const int p0 = offsets[e];
+    const int ne = offsets[e + 1] - p0;
+    if (ne == 0) continue;
+    const uint8_t *ex = packed + (size_t)e * expert_bytes;
     const int gg = 8 * b + wave;  // this wave's gate group
     const int grp[kGuGroups] = {gg, ngate + gg};
 
@@ -350,7 +353,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > 0) stage_barrier();  // previous chunk's readers are done with the rings
+        if (!first) stage_barrier();  // previous pass's readers are done with the rings
+        first = false;
         int unused[kGuGroups];
         with_tiles(mt, wave, [&](auto mtc, auto copies) {
             gu_pipeline<false, decltype(mtc)::value, decltype(copies)::value>(
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
             }
         }
     }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -384,14 +389,17 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h16,
     const int32_t *__restrict__ hexp, float *__restrict__ y) {
     __shared__ __align__(16) GuLds lds;
-    int e, b;
-    map_expert_block(blockIdx.x, E, H / 256, &e, &b);
-    const int p0 = offsets[e];
-    const int ne = offsets[e + 1] - p0;
-    if (ne == 0) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
+    const int nitems = E * (H / 256);
+    bool first = true;
+    for (int item = (int)blockIdx.x; item < nitems; item += (int)gridDim.x) {
+    int e, b;
+    map_expert_block(item, E, H / 256, &e, &b);
+    const int p0 = offsets[e];
+    const int ne = offsets[e + 1] - p0;
+    if (ne == 0) continue;
     const uint8_t *codes = packed + (size_t)e * expert_bytes + (size_t)I * H + (size_t)I * H / 16;
     const size_t kt = (size_t)(I / 32);
     const int grp[kGuGroups] = {16 * b + 2 * wave, 16 * b + 2 * wave + 1};
@@ -405,7 +413,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
         for (int g = 0; g < kGuGroups; ++g)
 #pragma unroll
             for (int t = 0; t < kGuTiles; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (c0 > 0) stage_barrier();
+        if (!first) stage_barrier();
+        first = false;
         int bexp[kGuGroups];
         with_tiles(mt, wave, [&](auto mtc, auto copies) {
             gu_pipeline<true, decltype(mtc)::value, decltype(copies)::value>(
@@ -430,11 +439,20 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
             }
         }
     }
+    }
+}
+
+// Persistent grid: one block per CU, a multiple of 8 when there is enough
+// work, so block b stays on XCD b % 8 and deals the items of that XCD.
+static int gu_grid(int items) {
+    int g = min(items, device_cu_count());
+    if (g >= 8) g &= ~7;
+    return max(g, 1);
 }
 
 hipError_t launch_prefill_gateup(const Shape &s, int T, const uint16_t *x, const uint8_t *packed,
                                  const Workspace &ws, hipStream_t st) {
-    prefill_gateup_mxfp4<<<s.E * (s.I / 128), kGuThreads, 0, st>>>(
+    prefill_gateup_mxfp4<<<gu_grid(s.E * (s.I / 128)), kGuThreads, 0, st>>>(
         x, packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm,
         static_cast<float *>(ws.h));
     return hipGetLastError();
@@ -444,7 +462,7 @@ hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, con
                                hipStream_t st) {
     hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
-    prefill_down_mxfp4<<<s.E * (s.H / 256), kGuThreads, 0, st>>>(
+    prefill_down_mxfp4<<<gu_grid(s.E * (s.H / 256)), kGuThreads, 0, st>>>(
         packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, ws.h16, ws.hexp, ws.y);
     return hipGetLastError();
 }
