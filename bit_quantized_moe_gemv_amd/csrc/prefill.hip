@@ -8,8 +8,8 @@
 // weights and multiplies it with all of the expert's tokens, up to 128 of them
 // per pass over the slice, so the slice leaves HBM once.
 //
-// Shape of a kernel: one block of eight waves per CU, at most 256 registers
-// per wave and 136 KiB of LDS.  Each wave owns 2 row groups (16 weight rows
+// Shape of a kernel: one persistent block of eight waves per CU, at most 256
+// registers per wave and 136 KiB of LDS.  Each wave owns 2 row groups (16 weight rows
 // each; for gate/up a gate group and its up partner) and all of the pass's
 // 16-token tiles, so no two waves load or dequantise the same weights.  Per K
 // step of 128 columns each wave issues, in a fixed order, its copies of the B
@@ -77,9 +77,10 @@ __device__ __forceinline__ void copy_lds4(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
-// blockIdx -> (expert, block): the blocks of one expert land on one XCD (the
-// dispatcher deals workgroups round-robin over the 8 XCDs), so the expert's
-// token rows and shared weight slices are re-read from that XCD's L2.
+// item -> (expert, block): the items of one expert go to blocks of one XCD
+// (the dispatcher deals workgroups round-robin over the 8 XCDs, and a block
+// takes the items congruent to its index mod 8), so the expert's token rows
+// and shared weight slices are re-read from that XCD's L2.
 __device__ __forceinline__ void map_expert_block(int bid, int E, int NB, int *e, int *blk) {
     if ((E & 7) == 0) {
         const int xcd = bid & 7, slot = bid >> 3;
@@ -115,10 +116,11 @@ __device__ __forceinline__ float e8m0_rel_f32(uint32_t e, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  Grid: E * I/128 blocks of 8 waves, one per CU.  Block b
-// of expert e owns gate row groups 8b..8b+7 and their up partners and all of
-// the expert's tokens, 128 per pass; wave w computes gate group 8b+w and its
-// up partner for every 16-token tile of the pass.  Per 128-column step every
+// gate/up + SwiGLU.  Persistent blocks of 8 waves, one per CU, loop over the
+// E * I/128 items; item (e, b) owns gate row groups 8b..8b+7 of expert e and
+// their up partners and all of the expert's tokens, 128 per pass; wave w
+// computes gate group 8b+w and its up partner for every 16-token tile of the
+// pass.  Per 128-column step every
 // wave issues its four 1 KiB pieces of the B stage, the scales of its 2
 // groups, then its 2 code loads, for the step three ahead, at a barrier in the
 // middle of the current step; branch-free, so the wait counts stay exact.
@@ -379,10 +381,10 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
 }
 
 // ---------------------------------------------------------------------------
-// down.  Grid: E * H/256 blocks of 8 waves, one per CU, on the same pipeline
-// with fp16 operands.  Block b owns output row groups 16b..16b+15 (wave w:
-// 16b+2w, +1) and all of the expert's tokens, 128 per pass; the h16 rows are
-// contiguous (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
+// down.  Persistent blocks of 8 waves, one per CU, over the E * H/256 items,
+// on the same pipeline with fp16 operands.  Item (e, b) owns output row groups
+// 16b..16b+15 (wave w: 16b+2w, +1) and all of the expert's tokens, 128 per
+// pass; the h16 rows are contiguous (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
