@@ -44,11 +44,12 @@ def test_tiny_vq_zero_router_multi_chunk(torch_dev):
     assert got["counts"][:2].tolist() == [150, 150]
 
 
-@pytest.mark.parametrize("t", [17, 32, 33, 64, 65, 96, 97, 128, 129])
+@pytest.mark.parametrize("t", [17, 32, 33, 48, 49, 64, 65, 80, 81, 96, 97, 112, 113, 128, 129])
 def test_tiny_vq_grouped_tile_counts(torch_dev, t):
     """A zero router gives experts 0 and 1 all t tokens (t > 16: the grouped
-    GEMM): each compiled token-tile count of a pass (2, 4, 6, 8 tiles of 16,
-    the pass's count rounded up to even) at its edges, and a second pass."""
+    GEMM): each compiled token-tile count of a pass (2 to 8 tiles of 16, a lone
+    tile run as two) at its edges, the switch from two K steps per LDS slot
+    (up to 112 tokens) to one (113 and more), and a second pass."""
     wl = W.TINY_VQ.replace(tokens=t, seed=300 + t)
     wr = np.zeros((wl.experts, wl.hidden), dtype=np.float32)
     got, _, _ = _full_check(torch_dev, wl, PRE, wr=wr)
@@ -112,3 +113,16 @@ def test_mimo_vq_verify_t16(torch_dev):
                             packed=W.make_experts(W.VQ_PREFILL))
     assert got["path"] == PRE
     assert 40 <= int((got["counts"] > 0).sum()) <= 128
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_VQ13R8, W.FMT_VQ13], ids=["vq13r8", "vq13"])
+@pytest.mark.parametrize("t", [5, 16])
+def test_vq_small_batch_chained_passes(torch_dev, fmt, t):
+    """Small batches (2..16 tokens) at a shape where both GEMMs have a multiple
+    of four 256-column super-steps (hidden 2048: 8, intermediate 1024: 4) and
+    the active experts give every block two or more items, so each block's
+    passes load their successors' first index streams; every row."""
+    wl = W.TINY_VQ.replace(hidden=2048, inter=1024, experts=128, top_k=8, tokens=t, fmt=fmt,
+                           seed=400 + t + 10 * fmt, name=f"vq_small_chain_{fmt}_{t}")
+    got, _, _ = _full_check(torch_dev, wl, PRE)
+    assert int((got["counts"] > 0).sum()) >= min(t * 8, 128) // 3
