@@ -221,6 +221,30 @@ __device__ __forceinline__ void vg_kstep(const uint32_t (&crn)[G][6], const L &l
     vg_form_a<RES>(cbv, rbv, a);
 }
 
+// The same K step with its B operands already in registers (bv, read one K
+// step earlier): it reads the next step's B from bqn into bv and gathers the
+// next step's book rows before its MFMAs, which therefore wait for nothing.
+template <int SN, int MT, bool RES, int G, class L>
+__device__ __forceinline__ void vg_kstep_pf(const uint32_t (&crn)[G][6], const L &lds,
+                                            const uint4 *bqn, int lane, f16x8 (&a)[G],
+                                            uint4 (&bv)[MT], f32x4 (&acc)[G][MT]) {
+    const int n = lane & 15;
+    uint4 bvn[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) bvn[t] = bqn[16 * t + n];
+    uint4 cbv[G], rbv[G];
+    vg_gather<SN, RES>(crn, lds, cbv, rbv);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            acc[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[g], __builtin_bit_cast(f16x8, bv[t]),
+                                                               acc[g][t], 0, 0, 0);
+    vg_form_a<RES>(cbv, rbv, a);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) bv[t] = bvn[t];
+}
+
 // The index streams of one item's rows: the code12, plane and residual
 // regions of its matrix and the wave's row groups.
 struct VgCodes {
@@ -292,23 +316,25 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
         }
     };
     auto slot_base = [&](int P) { return &lds.b[P & 1][0]; };
-    uint4 bst0, bst1;
-    auto load_b = [&](int P) {  // slot step P; this wave's K step S = KPS*P + kw
+    auto load_to = [&](int P, uint4 &r0, uint4 &r1) {  // slot step P; K step S = KPS*P + kw
         const int S = KPS * P + kw;
         const int off = 256 * (S >> 3) + 64 * sq + 8 * (S & 7);
-        bst0 = *reinterpret_cast<const uint4 *>(brow0 + off);
-        if constexpr (NL == 2) bst1 = *reinterpret_cast<const uint4 *>(brow1 + off);
+        r0 = *reinterpret_cast<const uint4 *>(brow0 + off);
+        if constexpr (NL == 2) r1 = *reinterpret_cast<const uint4 *>(brow1 + off);
     };
-    auto store_b = [&](int P) {
+    auto store_from = [&](int P, const uint4 &r0, const uint4 &r1) {
         uint4 *base = slot_base(P);
         if constexpr (KPS == 2) {
-            base[(kw * 4 + sq) * kVgPair + lane] = bst0;
+            base[(kw * 4 + sq) * kVgPair + lane] = r0;
             if constexpr (NL == 2)
-                if (64 + lane < kVgPair) base[(kw * 4 + sq) * kVgPair + 64 + lane] = bst1;
+                if (64 + lane < kVgPair) base[(kw * 4 + sq) * kVgPair + 64 + lane] = r1;
         } else {
-            base[sq * kVgChunk + 64 * (wave >> 2) + lane] = bst0;
+            base[sq * kVgChunk + 64 * (wave >> 2) + lane] = r0;
         }
     };
+    uint4 bst0, bst1;
+    auto load_b = [&](int P) { load_to(P, bst0, bst1); };
+    auto store_b = [&](int P) { store_from(P, bst0, bst1); };
     auto b_row = [&](int P, int kk) -> const uint4 * {  // K step kk of slot step P, piece q
         return slot_base(P) + (KPS == 2 ? (kk * 4 + q) * kVgPair : q * kVgChunk);
     };
@@ -317,7 +343,9 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
     vq_stage_barrier();  // the previous pass's readers are done with the ring
     const int NP = SPS * NJ, lastP = NP - 1;
     if (!have_first) issue_codes(0, 0);
-    load_b(0);
+    uint4 b00, b01, b10, b11;  // B of slot steps 0 and 1
+    load_to(0, b00, b01);
+    load_to(min(1, lastP), b10, b11);
     // The epilogue's operands travel with the first B rows: the gains of the
     // wave's two groups (rows 4q..4q+3) and, per token tile, the exponent of
     // the lane's token (MODE 0: through perm, so the exponent loads follow
@@ -334,21 +362,28 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
     if (MODE == 0)
 #pragma unroll
         for (int t = 0; t < MT; ++t) ex[t] = bexp[ex[t] / K];
-    store_b(0);
-    load_b(min(1, lastP));
+    store_from(0, b00, b01);
+    store_from(1, b10, b11);
+    load_b(min(2, lastP));
+    vq_stage_barrier();  // slots 0 and 1 published
     f16x8 a[kVgGroups];  // the A operands of the current K step
+    uint4 bv[MT];        // its B operands
     {
+        const uint4 *bq = b_row(0, 0);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) bv[t] = bq[16 * t + n];
         uint4 cbv[kVgGroups], rbv[kVgGroups];
         vg_gather<0, RES>(cr[0], lds, cbv, rbv);
         vg_form_a<RES>(cbv, rbv, a);
     }
-    // Per slot step P = SPS*J + p: the barrier publishes B(P) (stored at P-1)
-    // and, every wave being done with step P-1, frees the other slot; B(P+1)
-    // (issued at P-1, followed by the code loads of super-step J+1 when P-1
-    // began super-step J) lands and goes there; then B(P+2) and, at p = 0, the
-    // codes of super-step J+1 are issued.  The loads stay in flight through
-    // the barrier.  Loads are issued every step (indices clamped past the
-    // end), so the wait counts are exact.
+    // Per slot step P = SPS*J + p, before its last K step: a barrier publishes
+    // slot step P+1 (stored at P-1) and, every wave having read all of slot
+    // step P's B (each K step reads the next one's), frees slot P's buffer,
+    // where B(P+2) (issued at P-1, followed by the code loads of super-step
+    // J+1 when P-1 began super-step J) goes once it lands; then B(P+3) and, at
+    // p = 0, the codes of super-step J+1 are issued, and the last K step reads
+    // slot step P+1's first B.  Loads are issued every step (indices clamped
+    // past the end), so the wait counts are exact.
     for (int J0 = 0; J0 < NJ; J0 += 2) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -356,30 +391,34 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
 #pragma unroll
             for (int p = 0; p < SPS; ++p) {
                 const int P = SPS * J + p;
-                vq_stage_barrier();
-                if (p == 1)
-                    vq_wait_vmcnt<kCodeLoads>();
-                else
-                    vq_wait_vmcnt<0>();
-                store_b(min(P + 1, lastP));
-                load_b(min(P + 2, lastP));
-                if (p == 0) issue_codes(jj ^ 1, J + 1);
-                if (J < NJ) {
 #pragma unroll
-                    for (int kk = 0; kk < KPS; ++kk) {
-                        // K step s; the next one's codes: this super-step's,
-                        // or at s = 7 the next super-step's (issued at p = 0,
-                        // landed by p = 2; past the end they repeat the last)
+                for (int kk = 0; kk < KPS; ++kk) {
+                    if (kk == KPS - 1) {
+                        vq_stage_barrier();
+                        if (p == 1)
+                            vq_wait_vmcnt<kCodeLoads>();
+                        else
+                            vq_wait_vmcnt<0>();
+                        store_b(min(P + 2, lastP));
+                        load_b(min(P + 3, lastP));
+                        if (p == 0) issue_codes(jj ^ 1, J + 1);
+                    }
+                    if (J < NJ) {
+                        // K step s; the next one's B: this slot step's, or
+                        // after the last the next slot step's first; its
+                        // codes: this super-step's, or at s = 7 the next
+                        // super-step's (issued at p = 0, landed by p = 2;
+                        // past the end they repeat the last)
                         const int s = KPS * p + kk;
-                        const uint4 *bq = b_row(P, kk);
-                        if (s == 0) vg_kstep<1, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 1) vg_kstep<2, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 2) vg_kstep<3, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 3) vg_kstep<4, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 4) vg_kstep<5, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 5) vg_kstep<6, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 6) vg_kstep<7, MT, RES>(cr[jj], lds, bq, lane, a, acc);
-                        if (s == 7) vg_kstep<0, MT, RES>(cr[jj ^ 1], lds, bq, lane, a, acc);
+                        const uint4 *bqn = kk < KPS - 1 ? b_row(P, kk + 1) : b_row(P + 1, 0);
+                        if (s == 0) vg_kstep_pf<1, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 1) vg_kstep_pf<2, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 2) vg_kstep_pf<3, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 3) vg_kstep_pf<4, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 4) vg_kstep_pf<5, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 5) vg_kstep_pf<6, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 6) vg_kstep_pf<7, MT, RES>(cr[jj], lds, bqn, lane, a, bv, acc);
+                        if (s == 7) vg_kstep_pf<0, MT, RES>(cr[jj ^ 1], lds, bqn, lane, a, bv, acc);
                     }
                 }
             }
