@@ -575,7 +575,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
 // groups (G/2)(8*slice + w) + i, i < G/2, and their up partners), MODE 1 slice
 // = 128G output rows (wave w: groups G(8*slice + w) + g, clamped past the end
 // and never stored).  One 16-token tile, so the index streams carry the kernel:
-// they go to registers two super-steps ahead (a ring of three), and B, one
+// they go to registers two super-steps ahead (a ring of four, so a pass's
+// last two super-steps can load the next pass's first two), and B, one
 // super-step of 16 tokens (8 KiB), goes through two LDS slots, so a pass
 // meets one barrier per super-step.  The K steps run as in the grouped GEMM
 // (the next step's book rows gathered under the current step's MFMAs).
