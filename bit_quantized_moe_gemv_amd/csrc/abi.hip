@@ -90,6 +90,8 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
     ws->h = take(R * s.I * 4);
     ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
+    ws->y16 = reinterpret_cast<uint16_t *>(ws->y);
+    ws->yexp = reinterpret_cast<int8_t *>(ws->y16 + R * s.H);
     ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
     ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));
     ws->x16 = nullptr;

@@ -384,12 +384,14 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_gateup_mxfp4(
 // down.  Persistent blocks of 8 waves, one per CU, over the E * H/256 items,
 // on the same pipeline with fp16 operands.  Item (e, b) owns output row groups
 // 16b..16b+15 (wave w: 16b+2w, +1) and all of the expert's tokens, 128 per
-// pass; the h16 rows are contiguous (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p).
+// pass; the h16 rows are contiguous (route-position order).  y[p][row] = acc * 2^(b_g - 127 + s_p),
+// written as fp16 rows with an exponent per 16 rows (y16, yexp).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int E,
     const int32_t *__restrict__ offsets, const uint16_t *__restrict__ h16,
-    const int32_t *__restrict__ hexp, float *__restrict__ y) {
+    const int32_t *__restrict__ hexp, int ysh, uint16_t *__restrict__ y16,
+    int8_t *__restrict__ yexp) {
     __shared__ __align__(16) GuLds lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,6 +428,12 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
         int hs[kGuTiles];  // row exponents of the lane's tokens, fetched together
 #pragma unroll
         for (int t = 0; t < kGuTiles; ++t) hs[t] = hexp[p0 + c0 + min(16 * t + n, nt - 1)] - 127;
+        // y = acc * 2^(b_g + s_r), stored as fp16 times 2^ey per 16 output
+        // rows of a route, ey = b_g + s_r + ysh.  |acc| <= I * 6 * 2^15 (the
+        // A operand is at most 6 in magnitude, an h16 row's largest is below
+        // 2^15), so acc * 2^-ysh with ysh = ceil(log2(6 I)) stays below 2^15
+        // and every value at most 2^29 under that bound keeps fp16's 11
+        // significant bits.
 #pragma unroll
         for (int t = 0; t < kGuTiles; ++t) {
             const int m = 16 * t + n;
@@ -433,10 +441,13 @@ __global__ __launch_bounds__(kGuThreads, 1) void prefill_down_mxfp4(
                 const size_t p = (size_t)(p0 + c0 + m);
 #pragma unroll
                 for (int g = 0; g < kGuGroups; ++g) {
-                    const int sc = bexp[g] + hs[t];
-                    *reinterpret_cast<float4 *>(y + p * H + 16 * grp[g] + 4 * q) =
-                        make_float4(ldexpf(acc[g][t][0], sc), ldexpf(acc[g][t][1], sc),
-                                    ldexpf(acc[g][t][2], sc), ldexpf(acc[g][t][3], sc));
+                    const int ey = min(max(bexp[g] + hs[t] + ysh, -128), 127);
+                    const int sh = bexp[g] + hs[t] - ey;  // -ysh unless ey was clamped
+                    union { _Float16 h[4]; uint2 u; } r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) r.h[i] = (_Float16)ldexpf(acc[g][t][i], sh);
+                    *reinterpret_cast<uint2 *>(y16 + p * H + 16 * grp[g] + 4 * q) = r.u;
+                    if (q == 0) yexp[p * (H / 16) + grp[g]] = (int8_t)ey;
                 }
             }
         }
@@ -464,8 +475,10 @@ hipError_t launch_prefill_down(const Shape &s, int T, const uint8_t *packed, con
                                hipStream_t st) {
     hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
+    int ysh = 0;  // ceil(log2(6 I))
+    while ((1 << ysh) < 6 * s.I) ++ysh;
     prefill_down_mxfp4<<<gu_grid(s.E * (s.H / 256)), kGuThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, ws.h16, ws.hexp, ws.y);
+        packed, s.expert_bytes, s.H, s.I, s.E, ws.offsets, ws.h16, ws.hexp, ysh, ws.y16, ws.yexp);
     return hipGetLastError();
 }
 

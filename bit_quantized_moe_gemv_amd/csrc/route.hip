@@ -489,7 +489,8 @@ hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// combine: out[t] = sum_s w[t,s] * y[inv[t*K+s]], slots in order
+// combine: out[t] = sum_s w[t,s] * y[inv[t*K+s]], slots in order (VQ formats:
+// y in fp32)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const float *__restrict__ w,
@@ -515,8 +516,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     }
 }
 
+// The same for MXFP4 layers, whose per-route outputs are fp16 with an exponent
+// per 16 columns: y[p][j] = y16[p][j] * 2^yexp[p][j/16] (exact in fp32), then
+// the same fused multiply-adds in slot order.  A thread takes 8 columns.
+__global__ __launch_bounds__(256) void combine16_kernel(const uint16_t *__restrict__ y16,
+                                                        const int8_t *__restrict__ yexp,
+                                                        const float *__restrict__ w,
+                                                        const int32_t *__restrict__ inv, int H,
+                                                        int K, float *__restrict__ out) {
+    const int t = blockIdx.x;
+    float wk[kMaxTopK];
+    int pk[kMaxTopK];
+    for (int s = 0; s < K; ++s) {
+        wk[s] = w[(size_t)t * K + s];
+        pk[s] = inv[(size_t)t * K + s];
+    }
+    for (int j = threadIdx.x * 8; j < H; j += blockDim.x * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < K; ++s) {
+            union { uint4 u; _Float16 h[8]; } v;
+            v.u = *reinterpret_cast<const uint4 *>(y16 + (size_t)pk[s] * H + j);
+            const int ey = yexp[(size_t)pk[s] * (H / 16) + (j >> 4)];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk[s], ldexpf((float)v.h[i], ey), acc[i]);
+        }
+        float4 *o = reinterpret_cast<float4 *>(out + (size_t)t * H + j);
+        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
 hipError_t launch_combine(const Shape &s, int T, const Workspace &ws, float *out, hipStream_t st) {
-    combine_kernel<<<T, 256, 0, st>>>(ws.y, ws.w, ws.inv, s.H, s.K, out);
+    if (s.fmt == MOE_FMT_MXFP4)
+        combine16_kernel<<<T, 256, 0, st>>>(ws.y16, ws.yexp, ws.w, ws.inv, s.H, s.K, out);
+    else
+        combine_kernel<<<T, 256, 0, st>>>(ws.y, ws.w, ws.inv, s.H, s.K, out);
     return hipGetLastError();
 }
 
