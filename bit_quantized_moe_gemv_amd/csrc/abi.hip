@@ -61,7 +61,7 @@ size_t workspace_bytes(const Shape &s, int tmax) {
     b += align256(R * 4);                   // perm
     b += align256(R * 4);                   // inv
     b += align256(R * s.I * 4);             // h
-    b += align256(R * s.H * 4);             // y
+    b += align256(R * s.H * 2 + R * (s.H / 4));  // y16, yexp
     b += align256(R * s.I * 2);             // h16
     b += align256(R * 4);                   // hexp
     if (is_vq_format(s.fmt)) {
@@ -89,8 +89,7 @@ void carve_workspace(const Shape &s, int tmax, void *base, Workspace *ws) {
     ws->perm = reinterpret_cast<int32_t *>(take(R * 4));
     ws->inv = reinterpret_cast<int32_t *>(take(R * 4));
     ws->h = take(R * s.I * 4);
-    ws->y = reinterpret_cast<float *>(take(R * s.H * 4));
-    ws->y16 = reinterpret_cast<uint16_t *>(ws->y);
+    ws->y16 = reinterpret_cast<uint16_t *>(take(R * s.H * 2 + R * (s.H / 4)));
     ws->yexp = reinterpret_cast<int8_t *>(ws->y16 + R * s.H);
     ws->h16 = reinterpret_cast<uint16_t *>(take(R * s.I * 2));
     ws->hexp = reinterpret_cast<int32_t *>(take(R * 4));

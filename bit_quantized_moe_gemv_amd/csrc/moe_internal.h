@@ -49,11 +49,10 @@ struct Workspace {
     int32_t *perm;     // [Rmax]
     int32_t *inv;      // [Rmax]
     void *h;           // [Rmax][I] fp32
-    float *y;          // [Rmax][H] fp32 per-route expert outputs (VQ formats)
-    // MXFP4: the same memory holds the per-route outputs as fp16 times a power
-    // of two per 16 output rows: y = y16 * 2^yexp
-    uint16_t *y16;     // [Rmax][H], aliases the start of y
-    int8_t *yexp;      // [Rmax][H/16], aliases y after y16
+    // per-route expert outputs, fp16 times a power of two per 16 (MXFP4) or
+    // 4 (VQ) output rows: y = y16 * 2^yexp
+    uint16_t *y16;     // [Rmax][H]
+    int8_t *yexp;      // [Rmax][H/16] or [Rmax][H/4], after y16
     // fp16 rows with a power-of-two exponent each: h16/hexp feed the down GEMM
     // of both formats, x16/xexp (VQ only, null otherwise) the VQ gate/up GEMM
     uint16_t *x16;     // [Tmax][H]

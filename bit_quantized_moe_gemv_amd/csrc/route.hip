@@ -489,41 +489,18 @@ hipError_t launch_permute(const Shape &s, int T, const Workspace &ws, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// combine: out[t] = sum_s w[t,s] * y[inv[t*K+s]], slots in order (VQ formats:
-// y in fp32)
+// combine: out[t] = sum_s w[t,s] * y[inv[t*K+s]], slots in order.  The
+// per-route outputs are fp16 with an exponent per GW columns (16 for MXFP4,
+// 4 for the VQ formats): y[p][j] = y16[p][j] * 2^yexp[p][j/GW], exact in fp32,
+// then one fused multiply-add per slot.  A thread takes 8 columns.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+template <int GW>
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ y16,
+                                                      const int8_t *__restrict__ yexp,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv, int H, int K,
                                                       float *__restrict__ out) {
-    const int t = blockIdx.x;
-    float wk[kMaxTopK];
-    int pk[kMaxTopK];
-    for (int s = 0; s < K; ++s) {
-        wk[s] = w[(size_t)t * K + s];
-        pk[s] = inv[(size_t)t * K + s];
-    }
-    for (int j = threadIdx.x * 4; j < H; j += blockDim.x * 4) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < K; ++s) {
-            const float4 v = *reinterpret_cast<const float4 *>(y + (size_t)pk[s] * H + j);
-            acc.x = __builtin_fmaf(wk[s], v.x, acc.x);
-            acc.y = __builtin_fmaf(wk[s], v.y, acc.y);
-            acc.z = __builtin_fmaf(wk[s], v.z, acc.z);
-            acc.w = __builtin_fmaf(wk[s], v.w, acc.w);
-        }
-        *reinterpret_cast<float4 *>(out + (size_t)t * H + j) = acc;
-    }
-}
-
-// The same for MXFP4 layers, whose per-route outputs are fp16 with an exponent
-// per 16 columns: y[p][j] = y16[p][j] * 2^yexp[p][j/16] (exact in fp32), then
-// the same fused multiply-adds in slot order.  A thread takes 8 columns.
-__global__ __launch_bounds__(256) void combine16_kernel(const uint16_t *__restrict__ y16,
-                                                        const int8_t *__restrict__ yexp,
-                                                        const float *__restrict__ w,
-                                                        const int32_t *__restrict__ inv, int H,
-                                                        int K, float *__restrict__ out) {
+    static_assert(GW == 4 || GW == 16, "exponent group width");
     const int t = blockIdx.x;
     float wk[kMaxTopK];
     int pk[kMaxTopK];
@@ -536,9 +513,11 @@ __global__ __launch_bounds__(256) void combine16_kernel(const uint16_t *__restri
         for (int s = 0; s < K; ++s) {
             union { uint4 u; _Float16 h[8]; } v;
             v.u = *reinterpret_cast<const uint4 *>(y16 + (size_t)pk[s] * H + j);
-            const int ey = yexp[(size_t)pk[s] * (H / 16) + (j >> 4)];
+            const int8_t *ep = yexp + (size_t)pk[s] * (H / GW) + j / GW;
+            const int e0 = ep[0], e1 = GW == 4 ? ep[1] : e0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk[s], ldexpf((float)v.h[i], ey), acc[i]);
+            for (int i = 0; i < 8; ++i)
+                acc[i] = __builtin_fmaf(wk[s], ldexpf((float)v.h[i], i < 4 ? e0 : e1), acc[i]);
         }
         float4 *o = reinterpret_cast<float4 *>(out + (size_t)t * H + j);
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -547,10 +526,10 @@ __global__ __launch_bounds__(256) void combine16_kernel(const uint16_t *__restri
 }
 
 hipError_t launch_combine(const Shape &s, int T, const Workspace &ws, float *out, hipStream_t st) {
-    if (s.fmt == MOE_FMT_MXFP4)
-        combine16_kernel<<<T, 256, 0, st>>>(ws.y16, ws.yexp, ws.w, ws.inv, s.H, s.K, out);
+    if (is_vq_format(s.fmt))
+        combine_kernel<4><<<T, 256, 0, st>>>(ws.y16, ws.yexp, ws.w, ws.inv, s.H, s.K, out);
     else
-        combine_kernel<<<T, 256, 0, st>>>(ws.y, ws.w, ws.inv, s.H, s.K, out);
+        combine_kernel<16><<<T, 256, 0, st>>>(ws.y16, ws.yexp, ws.w, ws.inv, s.H, s.K, out);
     return hipGetLastError();
 }
 

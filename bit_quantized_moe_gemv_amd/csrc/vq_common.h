@@ -22,6 +22,20 @@ __device__ __forceinline__ int fp16_row_exponent(uint32_t maxbits) {
     return (e == 0 ? -126 : e - 127) - 14;
 }
 
+// Four consecutive values of a per-route output row -> fp16 times 2^ey, ey
+// putting their largest magnitude in [2^14, 2^15): y16[p][c..c+3] and
+// yexp[p][c/4] (c a multiple of 4).
+__device__ __forceinline__ void store_y16x4(uint16_t *__restrict__ y16, int8_t *__restrict__ yexp,
+                                            size_t p, int H, int c, const float (&v)[4]) {
+    const float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    const int ey = max((int)((__float_as_uint(mx) >> 23) & 0xFFu) - 141, -128);
+    union { _Float16 h[4]; uint2 u; } r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.h[i] = (_Float16)ldexpf(v[i], -ey);
+    *reinterpret_cast<uint2 *>(y16 + p * H + c) = r.u;
+    yexp[p * (H / 4) + c / 4] = (int8_t)ey;
+}
+
 // Block-wide maximum of non-negative fp32 bit patterns, compared as integers
 // (the same order as the magnitudes, subnormals included).  *slot must be 0
 // and visible to the block before the call.

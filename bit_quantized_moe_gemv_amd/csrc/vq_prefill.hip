@@ -266,7 +266,7 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
                                         const int32_t *__restrict__ perm,
                                         const uint16_t *__restrict__ bsrc,
                                         const int32_t *__restrict__ bexp,
-                                        float *__restrict__ out) {
+                                        float *__restrict__ out, int8_t *__restrict__ yexp) {
     const int(&grp)[kVgGroups] = cur.grp;
     const int q = lane >> 4, n = lane & 15;
     // An LDS slot holds two K steps of up to 112 tokens ([K step][piece
@@ -459,8 +459,7 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
                 float yv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) yv[j] = ldexpf(acc[g][t][j] * f16_bits_to_f32(gb[j]), hs);
-                *reinterpret_cast<float4 *>(out + (size_t)p * H + 16 * gg + 4 * q) =
-                    make_float4(yv[0], yv[1], yv[2], yv[3]);
+                store_y16x4(reinterpret_cast<uint16_t *>(out), yexp, (size_t)p, H, 16 * gg + 4 * q, yv);
             }
         }
     }
@@ -471,7 +470,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K, int E,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     const uint16_t *__restrict__ bsrc, const int32_t *__restrict__ bexp,
-    float *__restrict__ out) {
+    float *__restrict__ out, int8_t *__restrict__ yexp) {
     __shared__ __align__(16) VgLds lds;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_grouped_kernel(
         auto pass = [&](auto mtc) {
             vg_pass<MODE, decltype(mtc)::value, RES>(lds, cur.codes, cur.gain, nxt.codes, has_next,
                                                      have_first, cr, NJ, H, I, K, cur.p0 + c0, nt,
-                                                     wave, lane, perm, bsrc, bexp, out);
+                                                     wave, lane, perm, bsrc, bexp, out, yexp);
         };
         switch (mt) {
             case 1:
@@ -595,7 +594,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
     const uint8_t *__restrict__ packed, size_t expert_bytes, int H, int I, int K,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ active, const uint16_t *__restrict__ bsrc,
-    const int32_t *__restrict__ bexp, float *__restrict__ out) {
+    const int32_t *__restrict__ bexp, float *__restrict__ out, int8_t *__restrict__ yexp) {
     constexpr int G = vs_groups<RES>();
     constexpr int GG = G / 2;  // gate groups per wave (MODE 0)
     __shared__ __align__(16) VsLds lds;
@@ -792,8 +791,8 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             yv[j] = ldexpf(acc[g][0][j] * f16_bits_to_f32(gb[j]), ex);
-                        *reinterpret_cast<float4 *>(out + (size_t)p * H + 16 * gg + 4 * q) =
-                            make_float4(yv[0], yv[1], yv[2], yv[3]);
+                        store_y16x4(reinterpret_cast<uint16_t *>(out), yexp, (size_t)p, H,
+                                    16 * gg + 4 * q, yv);
                     }
                 }
             }
@@ -821,10 +820,12 @@ static void vg_launch(const Shape &s, const uint8_t *packed, const Workspace &ws
     const int grid = vq_grid(s.E * nslice);
     if (s.fmt == MOE_FMT_VQ13R8)
         vq_grouped_kernel<MODE, true><<<grid, kVqThreads, 0, st>>>(
-            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out);
+            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out,
+            ws.yexp);
     else
         vq_grouped_kernel<MODE, false><<<grid, kVqThreads, 0, st>>>(
-            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out);
+            packed, s.expert_bytes, s.H, s.I, s.K, s.E, ws.offsets, ws.perm, bsrc, bexp, out,
+            ws.yexp);
 }
 
 // items: at most min(T*K, E) active experts times the slices per expert
@@ -834,7 +835,8 @@ static void vs_launch(const Shape &s, int T, const uint8_t *packed, const Worksp
     constexpr int G = vs_groups<RES>();
     const int ns = MODE == 0 ? s.I / (64 * G) : (s.H + 128 * G - 1) / (128 * G);
     vq_small_kernel<MODE, RES><<<vq_grid(min(T * s.K, s.E) * ns), kVqThreads, 0, st>>>(
-        packed, s.expert_bytes, s.H, s.I, s.K, ws.offsets, ws.perm, ws.active, bsrc, bexp, out);
+        packed, s.expert_bytes, s.H, s.I, s.K, ws.offsets, ws.perm, ws.active, bsrc, bexp, out,
+        ws.yexp);
 }
 
 template <int MODE>
@@ -879,9 +881,9 @@ hipError_t launch_vq_prefill_down(const Shape &s, int T, const uint8_t *packed,
     hipError_t e = launch_hpack(s, T * s.K, ws, st);
     if (e != hipSuccess) return e;
     if (T <= kDecodeMaxTokens)
-        vs_launch<1>(s, T, packed, ws, ws.h16, ws.hexp, ws.y, st);
+        vs_launch<1>(s, T, packed, ws, ws.h16, ws.hexp, reinterpret_cast<float *>(ws.y16), st);
     else
-        vg_launch<1>(s, packed, ws, ws.h16, ws.hexp, ws.y, st);
+        vg_launch<1>(s, packed, ws, ws.h16, ws.hexp, reinterpret_cast<float *>(ws.y16), st);
     return hipGetLastError();
 }
 

@@ -232,7 +232,7 @@ int moe_read_probe(const void *buf, size_t bytes, size_t copy_stride, int32_t n_
  *   and alignment; out fully overwritten), enqueued on hip_stream
  * Returns MOE_EINVAL for a bad descriptor or argument, MOE_EWORKSPACE when
  * the workspace of T tokens (moe_workspace_size with max_tokens = T) exceeds
- * the array (at the MiMo shape: up to 72 tokens MXFP4, 69 VQ), MOE_EHIP when the address
+ * the array (at the MiMo shape: up to 96 tokens MXFP4, 91 VQ), MOE_EHIP when the address
  * lookup or a launch fails.  Makes no allocation of any kind.  All calls on
  * one GPU share its array, and a call leaves its contents behind (no kernel
  * reads workspace contents that the same call did not write first): calls

@@ -51,8 +51,9 @@ def test_sizes_for_the_mimo_layer(lib):
     assert bq.packed_size(256, 128, 8, 2) == 417792
     ws = bq.workspace_size(4096, 2048, 256, 8, 2048)
     r = 2048 * 8
-    # per route: h (fp32), y (fp32), the fp16 copy of h and its exponent
-    per_route = 2048 * 4 + 4096 * 4 + 2048 * 2 + 4
+    # per route: h (fp32), y (fp16 with one exponent byte per 4 or 16 columns),
+    # the fp16 copy of h and its exponent
+    per_route = 2048 * 4 + 4096 * 2 + 4096 // 4 + 2048 * 2 + 4
     assert ws >= r * per_route
     assert ws < r * per_route + 8 * 2**20
 
@@ -211,19 +212,19 @@ def test_binding_rejects_mismatched_tensors(lib):
 def test_noalloc_validates_before_any_device_call(lib):
     """moe_forward_noalloc checks its arguments and the workspace size before
     it touches a device: with no GPU here, reaching the device would return
-    MOE_EHIP, so these codes show the order.  73 MiMo-shaped tokens need more
+    MOE_EHIP, so these codes show the order.  97 MiMo-shaped tokens need more
     than the 16 MiB array."""
-    desc = bq.moe_layer_desc(4096, 2048, 256, 8, 80, 1, 0, 0)
+    desc = bq.moe_layer_desc(4096, 2048, 256, 8, 112, 1, 0, 0)
     p = 1 << 20  # aligned, never dereferenced
     f = lib.moe_forward_noalloc
-    assert bq.workspace_size(4096, 2048, 256, 8, 72) <= bq.MOE_NOALLOC_SCRATCH_BYTES
-    assert bq.workspace_size(4096, 2048, 256, 8, 73) > bq.MOE_NOALLOC_SCRATCH_BYTES
-    assert f(ctypes.byref(desc), p, 73, p, p, p, None) == bq.MOE_EWORKSPACE
+    assert bq.workspace_size(4096, 2048, 256, 8, 96) <= bq.MOE_NOALLOC_SCRATCH_BYTES
+    assert bq.workspace_size(4096, 2048, 256, 8, 97) > bq.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(desc), p, 97, p, p, p, None) == bq.MOE_EWORKSPACE
     assert f(ctypes.byref(desc), p, 0, p, p, p, None) == bq.MOE_EINVAL
-    assert f(ctypes.byref(desc), p, 81, p, p, p, None) == bq.MOE_EINVAL
+    assert f(ctypes.byref(desc), p, 113, p, p, p, None) == bq.MOE_EINVAL
     assert f(ctypes.byref(desc), p + 8, 4, p, p, p, None) == bq.MOE_EINVAL
     assert f(None, p, 4, p, p, p, None) == bq.MOE_EINVAL
-    bad = bq.moe_layer_desc(4096, 2048, 256, 9, 80, 1, 0, 0)
+    bad = bq.moe_layer_desc(4096, 2048, 256, 9, 112, 1, 0, 0)
     assert f(ctypes.byref(bad), p, 4, p, p, p, None) == bq.MOE_EINVAL
-    forced = bq.moe_layer_desc(4096, 2048, 256, 8, 80, 1, bq.MOE_PATH_DECODE, 0)
+    forced = bq.moe_layer_desc(4096, 2048, 256, 8, 112, 1, bq.MOE_PATH_DECODE, 0)
     assert f(ctypes.byref(forced), p, 17, p, p, p, None) == bq.MOE_EINVAL
