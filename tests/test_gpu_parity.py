@@ -181,6 +181,28 @@ def test_wide_exponent_spans(torch_dev, path, lo, hi):
     _full_check(torch_dev, wl, path)
 
 
+@pytest.mark.parametrize("path", [DEC, PRE], ids=["decode", "prefill"])
+def test_saturated_down_operands(torch_dev, path):
+    """Every weight +6 (the largest E2M1 value) at one scale and every token
+    0.9375: each h row is one value whose fp16 form lies just under 2^15, and
+    every down product is the largest the grouped down GEMM can meet, so its
+    fp32 sums reach 0.99 of the bound from which it scales the fp16 per-route
+    outputs (I * 6 * 2^15 * 2^-ceil(log2(6 I))).  The outputs stay finite and
+    match the oracle."""
+    from helpers import e2m1_table, mx_pack_expert
+    wl = W.TINY.replace(tokens=16 if path == DEC else 32, seed=17, name="tiny_saturated")
+    h, i, e = wl.hidden, wl.inter, wl.experts
+    six = int(np.nonzero(e2m1_table() == 6.0)[0][0])
+    one = mx_pack_expert(wl, np.full((2 * i, h), six), np.full((2 * i, h // 32), 127),
+                         np.full((h, i), six), np.full((h, i // 32), 127))
+    packed = np.tile(one, e)
+    x = np.full((wl.tokens, h), 0x3F70, dtype=np.uint16)  # bf16 0.9375
+    got, ref, _ = _full_check(torch_dev, wl, path, x=x, packed=packed)
+    g = 6.0 * h * 0.9375
+    hv = g / (1.0 + np.exp(-g)) * g
+    assert np.allclose(ref["out"], 6.0 * i * hv, rtol=1e-12)
+
+
 def test_prefill_long_down_rows(torch_dev):
     """Intermediate 2176: 68 scale tiles per down row, more than one pass of
     the per-group exponent scan, and 17 K steps."""
