@@ -286,10 +286,16 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_down_mxfp4(
     const uint32_t soff = (uint32_t)(q * 16 + n);
     float *hw = hs[wave];
 
-    for (int qs = wave >> 1; qs < n_active; qs += kDnWaves / 2) {
-        const int e = active[1 + qs];
-        const int p0 = single ? qs : offsets[e];
-        const int ne = single ? 1 : offsets[e + 1] - p0;
+    // the wave's slots qs = wave/2 + 8i (at most 32): lane i fetches slot i's
+    // expert and route range up front, so no slot waits on routing reads
+    const int qsl = (wave >> 1) + (kDnWaves / 2) * lane;
+    const int el = active[1 + min(qsl, n_active - 1)];
+    const int p0l = single ? qsl : offsets[el];
+    const int nel = single ? 1 : offsets[el + 1] - p0l;
+    for (int qs = wave >> 1, i = 0; qs < n_active; qs += kDnWaves / 2, ++i) {
+        const int e = __builtin_amdgcn_readlane(el, i);
+        const int p0 = __builtin_amdgcn_readlane(p0l, i);
+        const int ne = __builtin_amdgcn_readlane(nel, i);
         if (!live) {
             for (int r = 0; r < ne; ++r)
                 if (q == 0) ys[kh][p0 + r][n] = 0.f;
