@@ -114,10 +114,16 @@ __global__ __launch_bounds__(128 * KW) void decode_gateup_mxfp4(
         p0 = slot;
         ne = 1;
     } else {
-        if (slot >= active[0]) return;
-        e = active[1 + slot];
-        p0 = offsets[e];
-        ne = offsets[e + 1] - p0;
+        // routing reads through the vector unit, the lanes' loads together:
+        // lane 0 the active count, lane 1 the slot's expert, then lanes 0 and 1
+        // its route range
+        const int l = threadIdx.x & 63;
+        const int av = active[l == 0 ? 0 : 1 + min(slot, E - 1)];
+        if (slot >= __builtin_amdgcn_readlane(av, 0)) return;
+        e = __builtin_amdgcn_readlane(av, 1);
+        const int ov = offsets[e + (l & 1)];
+        p0 = __builtin_amdgcn_readlane(ov, 0);
+        ne = __builtin_amdgcn_readlane(ov, 1) - p0;
     }
     const int rg0 = blockIdx.y * RS;  // first of the block's RS row groups
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -323,13 +323,18 @@ __global__ __launch_bounds__(kVdThreads) void vq_dec_down(
 
     uint4 bv[kBookLoads];
     load_books<kVdThreads, RES>(packed, tid, bv);
+    // the routes' experts and weights: lane l (< 8) fetches route l's, each
+    // wave takes its two with readlane
+    const int pcl = min(lane, K - 1);
+    const int exl = active[1 + pcl];
+    const float wgl = wts[perm[pcl]];
     int ex[2];
     float wgt[2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {  // uniform: scalar loads
+    for (int f = 0; f < 2; ++f) {
         const int pc = min(4 * f + r4, K - 1);
-        ex[f] = active[1 + pc];
-        wgt[f] = wts[perm[pc]];
+        ex[f] = __builtin_amdgcn_readlane(exl, pc);
+        wgt[f] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgl), pc));
     }
     // h: thread t holds columns 4c..4c+3 (c = t mod I/4) of the routes of
     // phase hh = (t / (I/4)) & 1; threads past the first 2 * I/4 repeat them
