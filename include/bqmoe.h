@@ -97,7 +97,10 @@ enum { MOE_FMT_MXFP4 = 1, MOE_FMT_VQ13R8 = 2, MOE_FMT_VQ13 = 3 };
  * as fp16 rows scaled by an exact power of two per row (relative error
  * <= 2^-11).  The VQ decode kernels take Cb and
  * Rb unrounded and the activations as above.  All products accumulate in
- * fp32. */
+ * fp32.  The grouped path keeps each route's down output as fp16 times a power
+ * of two per 16 (MXFP4) or 4 (VQ) output rows (relative error <= 2^-11) and
+ * widens it exactly before the fp32 weighted combine; the decode kernels
+ * combine in fp32. */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
 #define MOE_DECODE_MAX_TOKENS 16
 
