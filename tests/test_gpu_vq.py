@@ -115,6 +115,19 @@ def test_mimo_vq_verify_t16(torch_dev):
     assert 40 <= int((got["counts"] > 0).sum()) <= 128
 
 
+@pytest.mark.parametrize("t", [3, 8])
+def test_mimo_vq_verify_widths(torch_dev, t):
+    """The narrower verify widths of the benchmark's sweep (3 drafted tokens,
+    and 8) on the MiMo-shaped VQ13R8 layer with the skewed router, AUTO path
+    (the small-batch kernel over the active experts); every row."""
+    from test_gpu_parity import _sampled_check
+    wl = W.VERIFY.replace(fmt=W.FMT_VQ13R8, tokens=t, name=f"mimo_vq_verify_t{t}_skewed")
+    got, _ = _sampled_check(torch_dev, wl, AUTO, list(range(t)),
+                            packed=W.make_experts(W.VQ_PREFILL))
+    assert got["path"] == PRE
+    assert got["counts"].sum() == t * wl.top_k
+
+
 @pytest.mark.parametrize("fmt", [W.FMT_VQ13R8, W.FMT_VQ13], ids=["vq13r8", "vq13"])
 @pytest.mark.parametrize("t", [5, 16])
 def test_vq_small_batch_chained_passes(torch_dev, fmt, t):
