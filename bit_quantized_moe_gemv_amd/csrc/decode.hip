@@ -44,8 +44,12 @@ constexpr int kRing = 4;  // 1 KiB wave loads kept in flight per wave
 // the compiler fall back to waiting for every outstanding load at the branch
 // joins, which serialises the weight stream.  Shapes are template parameters
 // and out-of-range staging loads are clamped duplicates instead of skipped.
+// Weights are read once per step: non-temporal loads, so they do not displace
+// the cached x, h and routing rows.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16(const uint8_t *base, uint32_t off) {
-    return *reinterpret_cast<const uint4 *>(base + off);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Empty asm register fences: the value becomes opaque at this point of the
