@@ -92,6 +92,14 @@ __device__ __forceinline__ void map_expert_block(int bid, int E, int NB, int *e,
     }
 }
 
+// 16 bytes per lane of a weight stream read once per forward: a non-temporal
+// load, so the codes do not displace the token rows re-read from L2.
+typedef uint32_t u32x4nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_nt(const uint8_t *p) {
+    const u32x4nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4nt *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -194,7 +202,7 @@ __device__ __forceinline__ void gu_pipeline(const uint8_t *codes, const uint8_t 
         copy_lds4(scales + soff + (size_t)J * 64, lds.sc[slot][wave]);
 #pragma unroll
         for (int g = 0; g < kGuGroups; ++g)
-            ring[slot][g] = *reinterpret_cast<const uint4 *>(codes + goff[g] + (size_t)J * 1024);
+            ring[slot][g] = ld16_nt(codes + goff[g] + (size_t)J * 1024);
     };
     const int last = nsuper - 1;
     issue(0, 0);

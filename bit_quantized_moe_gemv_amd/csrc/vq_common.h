@@ -65,6 +65,28 @@ __device__ __forceinline__ f16x8 add_f16x8(uint4 a, uint4 b) {
     return __builtin_bit_cast(f16x8, a) + __builtin_bit_cast(f16x8, b);
 }
 
+// A lane's index run of one 16 x 256 tile (12 code12 bytes, 8 res bytes or
+// zero, 1 plane byte), read with non-temporal loads: every index byte is read
+// once per forward, so it need not displace the cached rows and books.
+typedef uint32_t u32x2nt __attribute__((ext_vector_type(2)));
+template <bool RES>
+__device__ __forceinline__ void vq_load_run(const uint8_t *c12, const uint8_t *res,
+                                            const uint8_t *pln, size_t tile, int lane,
+                                            uint32_t (&c)[6]) {
+    const u32x3 a = __builtin_nontemporal_load(reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12));
+    c[0] = a.x;
+    c[1] = a.y;
+    c[2] = a.z;
+    if (RES) {
+        const u32x2nt r = __builtin_nontemporal_load(reinterpret_cast<const u32x2nt *>(res + tile * 512 + lane * 8));
+        c[3] = r.x;
+        c[4] = r.y;
+    } else {
+        c[3] = c[4] = 0;
+    }
+    c[5] = __builtin_nontemporal_load(pln + tile * 64 + lane);
+}
+
 // Byte regions of one VQ matrix of N rows and K columns; RES: the matrix
 // carries the residual index region (VQ13R8) or not (VQ13).
 template <bool RES>
@@ -81,18 +103,7 @@ struct VqMatrix {
     // lane's run of tile `tile`: 12 code12 bytes, 8 res bytes (zero without
     // the residual stage), 1 plane byte
     __device__ __forceinline__ void load(size_t tile, int lane, uint32_t (&c)[6]) const {
-        const u32x3 a = *reinterpret_cast<const u32x3 *>(c12 + tile * 768 + lane * 12);
-        c[0] = a.x;
-        c[1] = a.y;
-        c[2] = a.z;
-        if (RES) {
-            const uint2 r = *reinterpret_cast<const uint2 *>(res + tile * 512 + lane * 8);
-            c[3] = r.x;
-            c[4] = r.y;
-        } else {
-            c[3] = c[4] = 0;
-        }
-        c[5] = pln[tile * 64 + lane];
+        vq_load_run<RES>(c12, res, pln, tile, lane, c);
     }
 };
 

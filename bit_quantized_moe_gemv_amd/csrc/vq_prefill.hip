@@ -303,16 +303,7 @@ __device__ __forceinline__ void vg_pass(VgLds &lds, const VgCodes &cur, const ui
 #pragma unroll
         for (int g = 0; g < kVgGroups; ++g) {
             const size_t tile = (size_t)src.grp[g] * NJ + Js;
-            const u32x3 c = *reinterpret_cast<const u32x3 *>(src.c12 + tile * 768 + lane * 12);
-            uint2 r = make_uint2(0u, 0u);
-            if (RES) r = *reinterpret_cast<const uint2 *>(src.res + tile * 512 + lane * 8);
-            const uint32_t p = src.pln[tile * 64 + lane];
-            cr[slot][g][0] = c.x;
-            cr[slot][g][1] = c.y;
-            cr[slot][g][2] = c.z;
-            cr[slot][g][3] = r.x;
-            cr[slot][g][4] = r.y;
-            cr[slot][g][5] = p;
+            vq_load_run<RES>(src.c12, src.res, src.pln, tile, lane, cr[slot][g]);
         }
     };
     auto slot_base = [&](int P) { return &lds.b[P & 1][0]; };
@@ -685,16 +676,7 @@ __global__ __launch_bounds__(kVqThreads) void vq_small_kernel(
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const size_t tile = (size_t)src.grp[g] * NJ + Js;
-                    const u32x3 c = *reinterpret_cast<const u32x3 *>(src.c12 + tile * 768 + lane * 12);
-                    uint2 r = make_uint2(0u, 0u);
-                    if (RES) r = *reinterpret_cast<const uint2 *>(src.res + tile * 512 + lane * 8);
-                    const uint32_t pb = src.pln[tile * 64 + lane];
-                    cr[slot][g][0] = c.x;
-                    cr[slot][g][1] = c.y;
-                    cr[slot][g][2] = c.z;
-                    cr[slot][g][3] = r.x;
-                    cr[slot][g][4] = r.y;
-                    cr[slot][g][5] = pb;
+                    vq_load_run<RES>(src.c12, src.res, src.pln, tile, lane, cr[slot][g]);
                 }
             };
             uint4 bst;
